@@ -1,0 +1,370 @@
+// AR rejection sampling of the diffusion drafts, fused with the vocab-wide
+// softmax it needs (TiDAR review, awesome-system-papers wiki, 核心方法
+// section 3.2; acceptance rule of speculative sampling, Leviathan et al. 2023
+// and Chen et al. 2023: keep d_{i+1} with probability min(1, p_i/q_i), on the
+// first rejection draw from normalised max(0, p_i - q_i), after k acceptances
+// draw a bonus token from p_k).
+//
+// Three HBM-streaming launches, all with a fixed reduction order so results
+// are run-to-run deterministic:
+//   1. rej_stats : per (row, vocab chunk) max and sum of exp over the 2k+1
+//                  logit rows of each sequence (one read of all logits);
+//   2. rej_resid : every workgroup of a sequence merges the row statistics,
+//                  evaluates the acceptance chain from the gathered p_i(d),
+//                  q_i(d) (identical in all of them) and sums the residual
+//                  (or bonus) weights of its vocab chunk, in fp64;
+//   3. rej_pick  : per sequence, locates the chunk whose running mass passes
+//                  u * total, then the token inside it (inverse CDF in token
+//                  id order).
+#include "tidar_internal.h"
+
+#include <math.h>
+
+namespace tidar {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kChunk = 4096;            // vocab elements per chunk = 16 per thread
+constexpr int kPer = kChunk / kThreads;
+constexpr int kMaxK = 128;
+constexpr int kMaxChunks = 1024;
+constexpr float kNegInf = -INFINITY;
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sumf(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ __forceinline__ double wave_sumd(double x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Block reductions with a fixed combination order (waves 0..3 in sequence).
+__device__ __forceinline__ float block_max(float x, float* red) {
+  x = wave_max(x);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  __syncthreads();
+  if (l == 0) red[w] = x;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+__device__ __forceinline__ float block_sumf(float x, float* red) {
+  x = wave_sumf(x);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  __syncthreads();
+  if (l == 0) red[w] = x;
+  __syncthreads();
+  return ((red[0] + red[1]) + red[2]) + red[3];
+}
+__device__ __forceinline__ double block_sumd(double x, double* red) {
+  x = wave_sumd(x);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  __syncthreads();
+  if (l == 0) red[w] = x;
+  __syncthreads();
+  return ((red[0] + red[1]) + red[2]) + red[3];
+}
+
+__device__ __forceinline__ const float* row_ptr(const RejectParams& p, int b, int rr) {
+  // rows 0..k: AR logits (row i verifies d_{i+1}; row k is the bonus row);
+  // rows k+1..2k: diffusion logits of drafts 0..k-1
+  return rr <= p.k ? p.ar + ((size_t)b * (p.k + 1) + rr) * p.V
+                   : p.diff + ((size_t)b * p.k + (rr - p.k - 1)) * p.V;
+}
+
+// Load this thread's kPer elements of a chunk (scaled by 1/T); -inf past the end.
+__device__ __forceinline__ void load_chunk(const float* x, int e0, int e1, float inv_t, bool vec4,
+                                           float (&v)[kPer]) {
+  if (vec4 && e0 + kChunk <= e1) {
+#pragma unroll
+    for (int j = 0; j < kPer / 4; ++j) {
+      const float4 f = *reinterpret_cast<const float4*>(x + e0 + 4 * (threadIdx.x + kThreads * j));
+      v[4 * j + 0] = f.x * inv_t;
+      v[4 * j + 1] = f.y * inv_t;
+      v[4 * j + 2] = f.z * inv_t;
+      v[4 * j + 3] = f.w * inv_t;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int idx = e0 + threadIdx.x + kThreads * j;
+      v[j] = idx < e1 ? x[idx] * inv_t : kNegInf;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void rej_stats_kernel(RejectParams p) {
+  __shared__ float red[4];
+  const int c = blockIdx.x % p.nchunks;
+  const int row = blockIdx.x / p.nchunks;
+  const int nrows = 2 * p.k + 1;
+  const int b = row / nrows, rr = row % nrows;
+  const float* x = row_ptr(p, b, rr);
+  const int e0 = c * kChunk, e1 = min(e0 + kChunk, p.V);
+  float v[kPer];
+  load_chunk(x, e0, e1, p.inv_temp, (p.V & 3) == 0, v);
+  float mx = kNegInf;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) mx = fmaxf(mx, v[j]);
+  mx = block_max(mx, red);
+  float s = 0.f;
+  if (mx != kNegInf) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) s += expf(v[j] - mx);
+  }
+  s = block_sumf(s, red);
+  if (threadIdx.x == 0) p.row_stats[((size_t)b * nrows + rr) * p.nchunks + c] = make_float2(mx, s);
+}
+
+// Weight of token t for the final draw: residual max(0, p_n - q_n) after a
+// rejection, p_k for the bonus draw, p_n for the all-zero-residual fallback.
+struct DrawRows {
+  const float* a;  // AR row
+  const float* q;  // diffusion row, or nullptr for a plain AR draw
+  float ma, za, mq, zq;
+  __device__ __forceinline__ float w(float xa, float xq) const {
+    const float pa = expf(xa - ma) / za;
+    if (!q) return pa;
+    const float pq = expf(xq - mq) / zq;
+    return fmaxf(0.f, pa - pq);
+  }
+};
+
+// Merge the per-chunk statistics of row rr in chunk order.
+__device__ __forceinline__ float2 merge_row(const RejectParams& p, int b, int rr) {
+  const float2* st = p.row_stats + ((size_t)b * (2 * p.k + 1) + rr) * p.nchunks;
+  float m = kNegInf;
+  for (int c = 0; c < p.nchunks; ++c) m = fmaxf(m, st[c].x);
+  float z = 0.f;
+  if (m != kNegInf)
+    for (int c = 0; c < p.nchunks; ++c)
+      if (st[c].x != kNegInf) z += st[c].y * expf(st[c].x - m);
+  return make_float2(m, z);
+}
+
+__global__ __launch_bounds__(kThreads) void rej_resid_kernel(RejectParams p) {
+  __shared__ float2 mz[2 * kMaxK + 1];
+  __shared__ float rho[kMaxK];
+  __shared__ int n_sh;
+  __shared__ double redd[4];
+  const int c = blockIdx.x % p.nchunks, b = blockIdx.x / p.nchunks;
+  const int k = p.k, nrows = 2 * k + 1;
+  for (int rr = threadIdx.x; rr < nrows; rr += kThreads) {
+    const float2 v = merge_row(p, b, rr);
+    mz[rr] = v;
+    if (!(isfinite(v.x) && v.y > 0.f && isfinite(v.y)) && c == 0 && p.dev_status) atomicOr(p.dev_status, 8);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < k; i += kThreads) {
+    int d = p.drafts[(size_t)b * k + i];
+    float r = 0.f;
+    if (d < 0 || d >= p.V) {
+      if (c == 0 && p.dev_status) atomicOr(p.dev_status, 16);
+    } else {
+      const float2 sa = mz[i], sq = mz[k + 1 + i];
+      const float pa = expf(row_ptr(p, b, i)[d] * p.inv_temp - sa.x) / sa.y;
+      const float pq = expf(row_ptr(p, b, k + 1 + i)[d] * p.inv_temp - sq.x) / sq.y;
+      r = pq > 0.f ? pa / pq : INFINITY;
+    }
+    rho[i] = r;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int n = 0;
+    while (n < k) {
+      const float a = fminf(1.f, rho[n]);
+      if (p.uniforms[(size_t)b * (k + 1) + n] < a) ++n;
+      else break;
+    }
+    n_sh = n;
+  }
+  __syncthreads();
+  const int n = n_sh;
+  if (c == 0) {
+    for (int i = threadIdx.x; i < k; i += kThreads)
+      if (p.ratio) p.ratio[(size_t)b * k + i] = rho[i];
+    if (threadIdx.x == 0) {
+      p.accept_len[b] = n;
+      p.decision[2 * b] = n;
+      p.decision[2 * b + 1] = 0;
+    }
+  }
+  DrawRows dr;
+  dr.a = row_ptr(p, b, n);
+  dr.ma = mz[n].x;
+  dr.za = mz[n].y;
+  if (n < k) {
+    dr.q = row_ptr(p, b, k + 1 + n);
+    dr.mq = mz[k + 1 + n].x;
+    dr.zq = mz[k + 1 + n].y;
+  } else {
+    dr.q = nullptr;
+    dr.mq = 0.f;
+    dr.zq = 1.f;
+  }
+  const int e0 = c * kChunk, e1 = min(e0 + kChunk, p.V);
+  double acc = 0.0;
+  for (int j = 0; j < kPer; ++j) {
+    const int t = e0 + threadIdx.x + kThreads * j;
+    if (t < e1) acc += (double)dr.w(dr.a[t] * p.inv_temp, dr.q ? dr.q[t] * p.inv_temp : 0.f);
+  }
+  acc = block_sumd(acc, redd);
+  if (threadIdx.x == 0) p.resid_sums[(size_t)b * p.nchunks + c] = acc;
+}
+
+__global__ __launch_bounds__(kThreads) void rej_pick_kernel(RejectParams p) {
+  __shared__ double sums[kMaxChunks];
+  __shared__ double redd[4];
+  __shared__ double scan[kThreads];
+  __shared__ int pick_c;
+  __shared__ double pick_base;
+  __shared__ double target_sh;
+  __shared__ int first_t, last_pos;
+  const int b = blockIdx.x, k = p.k;
+  const int n = p.decision[2 * b];
+
+  // statistics of the rows used by the draw
+  __shared__ float2 sa, sq;
+  if (threadIdx.x == 0) sa = merge_row(p, b, n);
+  if (threadIdx.x == 1 && n < k) sq = merge_row(p, b, k + 1 + n);
+  __syncthreads();
+  DrawRows dr;
+  dr.a = row_ptr(p, b, n);
+  dr.ma = sa.x;
+  dr.za = sa.y;
+  if (n < k) {
+    dr.q = row_ptr(p, b, k + 1 + n);
+    dr.mq = sq.x;
+    dr.zq = sq.y;
+  } else {
+    dr.q = nullptr;
+    dr.mq = 0.f;
+    dr.zq = 1.f;
+  }
+
+  for (int c = threadIdx.x; c < p.nchunks; c += kThreads) sums[c] = p.resid_sums[(size_t)b * p.nchunks + c];
+  __syncthreads();
+  __shared__ double total_sh;
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+    for (int c = 0; c < p.nchunks; ++c) t += sums[c];
+    total_sh = t;
+  }
+  __syncthreads();
+  if (!(total_sh > 0.0)) {
+    // residual vanished through rounding: draw from p_n instead
+    dr.q = nullptr;
+    for (int c = 0; c < p.nchunks; ++c) {
+      const int e0 = c * kChunk, e1 = min(e0 + kChunk, p.V);
+      double acc = 0.0;
+      for (int j = 0; j < kPer; ++j) {
+        const int t = e0 + threadIdx.x + kThreads * j;
+        if (t < e1) acc += (double)dr.w(dr.a[t] * p.inv_temp, 0.f);
+      }
+      acc = block_sumd(acc, redd);
+      if (threadIdx.x == 0) sums[c] = acc;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      double t = 0.0;
+      for (int c = 0; c < p.nchunks; ++c) t += sums[c];
+      total_sh = t;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double target = (double)p.uniforms[(size_t)b * (k + 1) + k] * total_sh;
+    double run = 0.0;
+    int cf = -1, clast = 0;
+    double base = 0.0, base_last = 0.0;
+    for (int c = 0; c < p.nchunks; ++c) {
+      if (sums[c] > 0.0) { clast = c; base_last = run; }
+      if (cf < 0 && run + sums[c] > target) { cf = c; base = run; }
+      run += sums[c];
+    }
+    if (cf < 0) { cf = clast; base = base_last; }
+    pick_c = cf;
+    pick_base = base;
+    target_sh = target;
+    first_t = 0x7fffffff;
+    last_pos = -1;
+  }
+  __syncthreads();
+  // inverse CDF inside the chosen chunk: thread t owns kPer consecutive tokens
+  const int e0 = pick_c * kChunk, e1 = min(e0 + kChunk, p.V);
+  float w[kPer];
+  double mine = 0.0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int t = e0 + threadIdx.x * kPer + j;
+    w[j] = t < e1 ? dr.w(dr.a[t] * p.inv_temp, dr.q ? dr.q[t] * p.inv_temp : 0.f) : 0.f;
+    mine += (double)w[j];
+  }
+  scan[threadIdx.x] = mine;
+  __syncthreads();
+  if (threadIdx.x == 0) {  // exclusive scan in token order
+    double run = pick_base;
+    for (int i = 0; i < kThreads; ++i) {
+      const double x = scan[i];
+      scan[i] = run;
+      run += x;
+    }
+  }
+  __syncthreads();
+  double run = scan[threadIdx.x];
+  const double target = target_sh;
+  int mine_first = 0x7fffffff, mine_last = -1;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int t = e0 + threadIdx.x * kPer + j;
+    run += (double)w[j];
+    if (t < e1) {
+      if (run > target && mine_first == 0x7fffffff) mine_first = t;
+      if (w[j] > 0.f) mine_last = t;
+    }
+  }
+  if (mine_first != 0x7fffffff) atomicMin(&first_t, mine_first);
+  if (mine_last >= 0) atomicMax(&last_pos, mine_last);
+  __syncthreads();
+  if (threadIdx.x == 0) p.next_token[b] = first_t != 0x7fffffff ? first_t : max(last_pos, 0);
+}
+
+}  // namespace
+
+size_t reject_workspace_bytes(int B, int k, int V) {
+  const size_t nchunks = (size_t)(V + kChunk - 1) / kChunk;
+  size_t bytes = 0;
+  bytes += ((size_t)B * (2 * k + 1) * nchunks * sizeof(float2) + 255) / 256 * 256;
+  bytes += ((size_t)B * nchunks * sizeof(double) + 255) / 256 * 256;
+  bytes += ((size_t)B * 2 * sizeof(int32_t) + 255) / 256 * 256;
+  return bytes;
+}
+
+void plan_reject(RejectParams& p) {
+  p.chunk = kChunk;
+  p.nchunks = (p.V + kChunk - 1) / kChunk;
+}
+
+int reject_max_k() { return kMaxK; }
+int reject_max_chunks() { return kMaxChunks; }
+
+hipError_t launch_reject(const RejectParams& p, hipStream_t stream) {
+  const unsigned stats_grid = (unsigned)((size_t)p.nchunks * p.B * (2 * p.k + 1));
+  hipLaunchKernelGGL(rej_stats_kernel, dim3(stats_grid), dim3(kThreads), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(rej_resid_kernel, dim3((unsigned)((size_t)p.nchunks * p.B)), dim3(kThreads), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(rej_pick_kernel, dim3(p.B), dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace tidar

@@ -1,0 +1,79 @@
+// Internal declarations shared by the libtidar translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tidar {
+
+// Parameters of one hybrid-mask attention launch (one layer).
+struct AttnParams {
+  const void* q;
+  const void* k_step;
+  const void* v_step;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* cache_len;
+  void* out;
+  float* lse;
+  int32_t* dev_status;
+  float* part_o;   // [S, B, R, Hq, D] unnormalised partial outputs (S > 1 only)
+  float* part_ml;  // [S, B, R, Hq, 2] running max (log2 domain) and sum
+  int B, Hq, Hkv, D, g, R, k, num_blocks, block_len, cap, max_len;
+  int S;          // number of prefix splits
+  int chunk;      // prefix keys per split
+  int qtiles;     // query tiles per (b, kv head)
+  float sm_scale;
+  float scale_log2;  // sm_scale * log2(e)
+};
+
+struct AttnPlan {
+  int S;
+  int chunk;
+  int qtiles;
+  int bm;          // packed query rows per workgroup
+  size_t ws_bytes;
+};
+
+AttnPlan plan_attn(int dtype, int B, int Hq, int Hkv, int D, int R, int max_len, int forced_splits);
+hipError_t launch_attn_bf16(const AttnParams& p, hipStream_t stream);
+hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream);
+
+struct CommitParams {
+  int L, B, Hkv, D, k, step_rows, cap, elem_bytes;
+  const void* k_step;
+  const void* v_step;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* accept_len;
+  const int32_t* len_in;
+  int32_t* len_out;
+  int32_t* dev_status;
+};
+hipError_t launch_kv_commit(const CommitParams& p, hipStream_t stream);
+
+struct RejectParams {
+  int B, k, V;
+  int chunk;     // vocabulary elements per stats chunk
+  int nchunks;
+  const float* ar;
+  const float* diff;
+  const int32_t* drafts;
+  const float* uniforms;
+  float inv_temp;
+  int32_t* accept_len;
+  int32_t* next_token;
+  float* ratio;
+  int32_t* dev_status;
+  float2* row_stats;    // [B, 2k+1, nchunks] (max, sum exp) per chunk
+  double* resid_sums;   // [B, nchunks] residual (or bonus) mass per chunk
+  int32_t* decision;    // [B, 2]: accept length, source row kind
+};
+size_t reject_workspace_bytes(int B, int k, int V);
+int reject_max_k();
+int reject_max_chunks();
+void plan_reject(RejectParams& p);
+hipError_t launch_reject(const RejectParams& p, hipStream_t stream);
+
+}  // namespace tidar

@@ -262,3 +262,52 @@ def config_sampler(n: int, *, seed: int = 0, diff_sigma: float | None = None,
         s["diff_sigma"] = diff_sigma
     return sampler_case(batch=c["batch"] if batch is None else batch, k=c["k"],
                         vocab=c["vocab"], seed=seed + 1, **s)
+
+
+def fill_device_step(step, *, seed: int, cache_len, ar_sigma: float = 3.0,
+                     diff_sigma: float = 1.0, temperature: float = 1.0) -> None:
+    """Fill the buffers of a decode step on its device with a seeded torch RNG.
+
+    Same recipe as the numpy generators (Q/K/V ~ N(0, 1) rounded to the
+    buffer dtype, AR logits ~ N(0, ar_sigma), diffusion logits = AR + N(0,
+    diff_sigma), drafts by Gumbel-max from the diffusion logits, uniforms in
+    [0, 1)), but drawn on the GPU so full-depth workloads set up in seconds.
+    Cache rows at or beyond each sequence's length are left as NaN.
+    """
+    import torch
+
+    dev = step.q.device
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+
+    def normal_(t):
+        if t.dtype == torch.bfloat16:
+            # draw in fp32, round once to bf16
+            for i in range(t.shape[0]):
+                t[i].copy_(torch.randn(t[i].shape, generator=g, device=dev, dtype=torch.float32))
+        else:
+            t.normal_(generator=g)
+
+    for t in (step.q, step.k_step, step.v_step, step.k_cache, step.v_cache):
+        normal_(t)
+    lens = torch.as_tensor(np.broadcast_to(np.asarray(cache_len, np.int32), (step.B,)).copy())
+    step.cache_len.copy_(lens.to(dev))
+    step.cache_len_out.copy_(lens.to(dev))
+    pos = torch.arange(step.cap, device=dev)
+    invalid = pos[None, :] >= step.cache_len[:, None]          # [B, cap]
+    mask = invalid[None, :, None, :, None]
+    step.k_cache.masked_fill_(mask, float("nan"))
+    step.v_cache.masked_fill_(mask, float("nan"))
+    step.ar_logits.normal_(generator=g).mul_(ar_sigma)
+    k = step.k
+    if k:
+        noise = torch.randn(step.diff_logits.shape, generator=g, device=dev) * diff_sigma
+        step.diff_logits.copy_(step.ar_logits[:, :k] + noise)
+        u = torch.rand(step.diff_logits.shape, generator=g, device=dev).clamp_min(1e-30)
+        gumbel = -torch.log(-torch.log(u))
+        step.drafts.copy_(torch.argmax(step.diff_logits / temperature + gumbel, dim=-1).to(torch.int32))
+        del noise, u, gumbel
+    step.uniforms.copy_(torch.rand(step.uniforms.shape, generator=g, device=dev))
+    step.accept_len.zero_()
+    step.next_token.zero_()
+    step.dev_status.zero_()
