@@ -24,6 +24,7 @@ struct AttnParams {
   int S;          // number of prefix splits
   int chunk;      // prefix keys per split
   int qtiles;     // query tiles per (b, kv head)
+  int nqt;        // 32-row query tiles per wave (bf16 path)
   float sm_scale;
   float scale_log2;  // sm_scale * log2(e)
 };
@@ -32,6 +33,7 @@ struct AttnPlan {
   int S;
   int chunk;
   int qtiles;
+  int nqt;
   int bm;          // packed query rows per workgroup
   size_t ws_bytes;
 };
