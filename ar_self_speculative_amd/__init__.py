@@ -5,14 +5,14 @@ The compute runs in the HIP library ``libtidar.so`` (C ABI in
 Importing it without the built library raises ImportError.
 """
 from ._lib import (  # noqa: F401
-    AttnDesc, TidarError, attn_step, attn_workspace_bytes, kv_commit, last_error, load,
+    AttnDesc, TidarError, attn_step, attn_workspace, attn_workspace_bytes, kv_commit, last_error, load,
     make_attn_desc, reject_sample, reject_workspace_bytes, DTYPE_BF16, DTYPE_F32, EXPORTS,
     LIB_PATH,
 )
 from .step import DecodeStep  # noqa: F401
 
 __all__ = [
-    "AttnDesc", "TidarError", "attn_step", "attn_workspace_bytes", "kv_commit", "last_error",
+    "AttnDesc", "TidarError", "attn_step", "attn_workspace", "attn_workspace_bytes", "kv_commit", "last_error",
     "make_attn_desc", "reject_sample", "reject_workspace_bytes", "DecodeStep", "DTYPE_BF16",
     "DTYPE_F32", "EXPORTS", "LIB_PATH",
 ]

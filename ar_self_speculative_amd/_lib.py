@@ -56,7 +56,7 @@ class TidarError(RuntimeError):
 
 def load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m ar_self_speculative_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python ar_self_speculative_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     lib.tidar_status_string.restype = ctypes.c_char_p
@@ -134,6 +134,14 @@ def make_attn_desc(*, batch, num_q_heads, num_kv_heads, head_dim, k, num_blocks,
 
 def attn_workspace_bytes(desc: AttnDesc) -> int:
     return int(_lib.tidar_attn_workspace_bytes(ctypes.byref(desc)))
+
+
+def attn_workspace(desc: AttnDesc, device="cuda"):
+    """A workspace tensor for ``desc`` (None when none is needed)."""
+    n = attn_workspace_bytes(desc)
+    if n == 0:
+        return None
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 def attn_step(desc: AttnDesc, q, k_step, v_step, k_cache, v_cache, cache_len, out, lse=None,

@@ -1,6 +1,7 @@
 """Build libtidar.so in-tree with hipcc for gfx950.
 
-Usage: ``python -m ar_self_speculative_amd.build`` (always recompiles).
+Usage: ``python ar_self_speculative_amd/build.py`` (always recompiles). Run it
+as a script, not through the package: importing the package loads the library.
 """
 from __future__ import annotations
 

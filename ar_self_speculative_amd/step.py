@@ -54,8 +54,7 @@ class DecodeStep:
         self.next_token = torch.zeros(B, dtype=torch.int32, device=dev)
         self.ratio = torch.zeros((B, k), dtype=torch.float32, device=dev)
         self.dev_status = torch.zeros(1, dtype=torch.int32, device=dev)
-        ab = _lib.attn_workspace_bytes(self.desc)
-        self.attn_ws = torch.empty(max(ab, 256), dtype=torch.uint8, device=dev) if ab else None
+        self.attn_ws = _lib.attn_workspace(self.desc, dev)
         rb = _lib.reject_workspace_bytes(B, k, vocab)
         self.rej_ws = torch.empty(max(rb, 256), dtype=torch.uint8, device=dev)
 

@@ -41,7 +41,7 @@ def run_attn(case, layer=0, num_splits=0, cache_len=None, max_cache_len=None, wi
     lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     wsb = tidar.attn_workspace_bytes(desc)
-    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device="cuda") if wsb else None
+    ws = torch.zeros(max(wsb, 256), dtype=torch.uint8, device="cuda") if wsb else None
     tidar.attn_step(desc, q, ks, vs, kc, vc, lens, out, lse, status, ws)
     torch.cuda.synchronize()
     res = (out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64))

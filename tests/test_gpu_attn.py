@@ -137,3 +137,19 @@ def test_cache_len_beyond_bound_is_clamped_and_flagged():
     ref, _ = _oracle_full(c, cache_len=[100])
     assert status & 1
     assert np.abs(out - ref).max() <= TOL["bf16"]
+
+
+def test_repeated_calls_on_one_workspace_agree():
+    import ar_self_speculative_amd as tidar
+    from tests.gpu_util import attn_desc, dev_array
+    c = config_attn(2, seed=4)
+    desc = attn_desc(c, num_splits=4)
+    args = [dev_array(c, n, 0) for n in ("q", "k_step", "v_step", "k_cache", "v_cache")]
+    lens = torch.from_numpy(c.cache_len).cuda()
+    ws = tidar.attn_workspace(desc)
+    outs = []
+    for _ in range(3):
+        out = torch.empty_like(args[0])
+        tidar.attn_step(desc, *args, lens, out, None, None, ws)
+        outs.append(out.float().cpu().numpy())
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
