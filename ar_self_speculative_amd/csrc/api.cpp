@@ -144,9 +144,10 @@ int tidar_attn_step(const tidar_attn_desc* desc, const void* q, const void* k_st
   p.scale_log2 = desc->sm_scale * 1.4426950408889634f;
   if (plan.S > 1) {
     const size_t rows = (size_t)plan.S * p.B * p.R * p.Hq;
-    p.part_o = static_cast<float*>(workspace);
-    const size_t o_bytes = (rows * p.D * sizeof(float) + 255) / 256 * 256;
-    p.part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+    const size_t elem = desc->dtype == TIDAR_DTYPE_BF16 ? 2 : 4;
+    p.part_o = workspace;
+    const size_t o_bytes = (rows * p.D * elem + 255) / 256 * 256;
+    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = desc->dtype == TIDAR_DTYPE_BF16 ? tidar::launch_attn_bf16(p, s) : tidar::launch_attn_f32(p, s);
@@ -238,10 +239,12 @@ int tidar_reject_sample(int32_t batch, int32_t k, int32_t vocab, const float* ar
   p.dev_status = dev_status;
   char* ws = static_cast<char*>(workspace);
   const size_t a = ((size_t)batch * (2 * k + 1) * p.nchunks * sizeof(float2) + 255) / 256 * 256;
-  const size_t bsz = ((size_t)batch * p.nchunks * sizeof(double) + 255) / 256 * 256;
+  const size_t bsz = ((size_t)2 * batch * p.nchunks * sizeof(double) + 255) / 256 * 256;
   p.row_stats = reinterpret_cast<float2*>(ws);
   p.resid_sums = reinterpret_cast<double*>(ws + a);
   p.decision = reinterpret_cast<int32_t*>(ws + a + bsz);
+  const size_t dsz = ((size_t)batch * 2 * sizeof(int32_t) + 255) / 256 * 256;
+  p.row_mz = reinterpret_cast<float2*>(ws + a + bsz + dsz);
   hipError_t e = tidar::launch_reject(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "reject launch");
   return TIDAR_OK;

@@ -13,11 +13,12 @@
 // S^T = K . Q^T, with v_mfma_f32_32x32x16_bf16, so each lane owns one query
 // row and 16 keys per 32-key sub-tile: the row maximum is an in-lane max
 // plus one half-wave swap (v_permlane32_swap), and the probabilities are
-// already in the B-operand layout of the O^T = V^T . P^T product. K tiles are
-// staged row-major in LDS, V tiles transposed. The prefix is split across
-// workgroups; partial (max, sum, unnormalised output) triples are merged by
-// log-sum-exp in a second kernel. The split that owns the last prefix keys
-// also processes the step's own keys under the region predicate.
+// already in the B-operand layout of the O^T = V^T . P^T product. K and V
+// tiles are staged row-major in LDS; V fragments are read with the
+// transposing ds_read_tr16_b64. The prefix is split across workgroups; each
+// split stores its normalised output (in the input precision) and its
+// log-sum-exp, and a second kernel merges them. The split that owns the last
+// prefix keys also processes the step's own keys under the region predicate.
 #include "tidar_internal.h"
 
 #include <math.h>
@@ -487,17 +488,23 @@ __global__ __launch_bounds__(kThreads, NQT == 1 ? 2 : 1) void attn_bf16_kernel(A
         }
       if (p.lse && half == 0) p.lse[orow] = (st.m[nt] + log2f(ltot)) * 0.69314718055994531f;
     } else {
+      // normalised partial in bf16 plus its log2-domain log-sum-exp
       const size_t prow = (size_t)s * p.B * p.R * p.Hq + orow;
-      float* po = p.part_o + prow * D;
+      const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+      u16* po = reinterpret_cast<u16*>(p.part_o) + prow * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int d = 32 * dt + 8 * i + 4 * half;
-          *reinterpret_cast<float4*>(po + d) = make_float4(st.o[nt][dt][4 * i + 0], st.o[nt][dt][4 * i + 1],
-                                                           st.o[nt][dt][4 * i + 2], st.o[nt][dt][4 * i + 3]);
+          ushort4 pk;
+          pk.x = f32_to_bf16_bits(st.o[nt][dt][4 * i + 0] * inv);
+          pk.y = f32_to_bf16_bits(st.o[nt][dt][4 * i + 1] * inv);
+          pk.z = f32_to_bf16_bits(st.o[nt][dt][4 * i + 2] * inv);
+          pk.w = f32_to_bf16_bits(st.o[nt][dt][4 * i + 3] * inv);
+          *reinterpret_cast<ushort4*>(po + d) = pk;
         }
-      if (half == 0) *reinterpret_cast<float2*>(p.part_ml + prow * 2) = make_float2(st.m[nt], ltot);
+      if (half == 0) p.part_lse[prow] = ltot > 0.f ? st.m[nt] + log2f(ltot) : kNegInf;
     }
   }
 }
@@ -613,62 +620,78 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p) {
     if (p.lse && lane == 0) p.lse[orow] = (mrow + log2f(lrow)) * 0.69314718055994531f;
   } else {
     const size_t prow = (size_t)s * p.B * p.R * p.Hq + orow;
+    const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
+    float* po = reinterpret_cast<float*>(p.part_o) + prow * D;
 #pragma unroll
     for (int j = 0; j < kF32MaxD / 64; ++j) {
       const int d = lane + 64 * j;
-      if (d < D) p.part_o[prow * D + d] = o[j];
+      if (d < D) po[d] = o[j] * inv;
     }
-    if (lane == 0) *reinterpret_cast<float2*>(p.part_ml + prow * 2) = make_float2(mrow, lrow);
+    if (lane == 0) p.part_lse[prow] = lrow > 0.f ? mrow + log2f(lrow) : kNegInf;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Log-sum-exp merge of the split partials: m = max_s m_s,
-// l = sum_s l_s 2^(m_s - m), O = sum_s o_s 2^(m_s - m) / l.
-// One thread per 4 output elements of a row.
+// Log-sum-exp merge of the split partials (normalised outputs o_s with
+// log2-domain log-sum-exps e_s): with w_s = 2^(e_s - max e),
+// O = sum_s w_s o_s / sum_s w_s and LSE = max e + log2(sum_s w_s).
+// One thread per 8 (bf16) or 4 (fp32) output elements of a row.
 // ---------------------------------------------------------------------------
 template <bool BF16>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
+  constexpr int VEC = BF16 ? 8 : 4;
   const int D = p.D;
-  const int tpr = D / 4;  // threads per row
+  const int tpr = D / VEC;  // threads per row
   const size_t rows = (size_t)p.B * p.R * p.Hq;
   const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   const size_t row = gid / tpr;
-  const int d = (int)(gid % tpr) * 4;
+  const int d = (int)(gid % tpr) * VEC;
   if (row >= rows) return;
-  float mmax = kNegInf;
-  for (int s = 0; s < p.S; ++s) mmax = fmaxf(mmax, p.part_ml[((size_t)s * rows + row) * 2]);
-  const float muse = (mmax == kNegInf) ? 0.f : mmax;
-  float l = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float emax = kNegInf;
+  for (int s = 0; s < p.S; ++s) emax = fmaxf(emax, p.part_lse[(size_t)s * rows + row]);
+  const float euse = (emax == kNegInf) ? 0.f : emax;
+  float wsum = 0.f;
+  float acc[VEC];
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
+#pragma unroll 4
   for (int s = 0; s < p.S; ++s) {
-    const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + ((size_t)s * rows + row) * 2);
-    if (ml.y == 0.f) continue;
-    const float wgt = exp2f(ml.x - muse);
-    l += ml.y * wgt;
-    const float4 o = *reinterpret_cast<const float4*>(p.part_o + ((size_t)s * rows + row) * D + d);
-    acc.x = fmaf(o.x, wgt, acc.x);
-    acc.y = fmaf(o.y, wgt, acc.y);
-    acc.z = fmaf(o.z, wgt, acc.z);
-    acc.w = fmaf(o.w, wgt, acc.w);
+    const size_t prow = (size_t)s * rows + row;
+    const float wgt = __builtin_amdgcn_exp2f(p.part_lse[prow] - euse);  // 0 for an empty split
+    wsum += wgt;
+    if (BF16) {
+      const uint4 raw = *reinterpret_cast<const uint4*>(reinterpret_cast<const u16*>(p.part_o) + prow * D + d);
+      const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = fmaf(__uint_as_float(w4[i] << 16), wgt, acc[2 * i]);
+        acc[2 * i + 1] = fmaf(__uint_as_float(w4[i] & 0xffff0000u), wgt, acc[2 * i + 1]);
+      }
+    } else {
+      const float4 o = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.part_o) + prow * D + d);
+      acc[0] = fmaf(o.x, wgt, acc[0]);
+      acc[1] = fmaf(o.y, wgt, acc[1]);
+      acc[2] = fmaf(o.z, wgt, acc[2]);
+      acc[VEC - 1] = fmaf(o.w, wgt, acc[VEC - 1]);
+    }
   }
-  const float inv = 1.f / l;
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   if (BF16) {
-    ushort4 pk;
-    pk.x = f32_to_bf16_bits(acc.x * inv);
-    pk.y = f32_to_bf16_bits(acc.y * inv);
-    pk.z = f32_to_bf16_bits(acc.z * inv);
-    pk.w = f32_to_bf16_bits(acc.w * inv);
-    *reinterpret_cast<ushort4*>(reinterpret_cast<u16*>(p.out) + row * D + d) = pk;
+    uint4 pk;
+    uint32_t* w4 = reinterpret_cast<uint32_t*>(&pk);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w4[i] = (uint32_t)f32_to_bf16_bits(acc[2 * i] * inv) | ((uint32_t)f32_to_bf16_bits(acc[2 * i + 1] * inv) << 16);
+    *reinterpret_cast<uint4*>(reinterpret_cast<u16*>(p.out) + row * D + d) = pk;
   } else {
     *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + row * D + d) =
-        make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+        make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[VEC - 1] * inv);
   }
-  if (p.lse && d == 0) p.lse[row] = (mmax + log2f(l)) * 0.69314718055994531f;
+  if (p.lse && d == 0) p.lse[row] = (emax + log2f(wsum)) * 0.69314718055994531f;
 }
 
 hipError_t launch_merge(const AttnParams& p, bool bf16, hipStream_t stream) {
-  const size_t threads = (size_t)p.B * p.R * p.Hq * (p.D / 4);
+  const size_t threads = (size_t)p.B * p.R * p.Hq * (p.D / (bf16 ? 8 : 4));
   const unsigned grid = (unsigned)((threads + 255) / 256);
   if (bf16)
     hipLaunchKernelGGL(attn_merge_kernel<true>, dim3(grid), dim3(256), 0, stream, p);
@@ -715,7 +738,10 @@ AttnPlan plan_attn(int dtype, int B, int Hq, int Hkv, int D, int R, int max_len,
   S = max_len > 0 ? (max_len + chunk - 1) / chunk : 1;
   pl.S = S;
   pl.chunk = chunk;
-  pl.ws_bytes = S > 1 ? (size_t)S * B * R * Hq * (size_t)(D + 2) * sizeof(float) + 256 : 0;
+  // partial outputs in the input precision, then one fp32 log-sum-exp per row
+  const size_t prow = (size_t)S * B * R * Hq;
+  const size_t elem = dtype == 1 ? 2 : 4;
+  pl.ws_bytes = S > 1 ? (prow * D * elem + 255) / 256 * 256 + prow * sizeof(float) : 0;
   return pl;
 }
 

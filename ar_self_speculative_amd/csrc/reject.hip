@@ -12,7 +12,8 @@
 //   2. rej_resid : every workgroup of a sequence merges the row statistics,
 //                  evaluates the acceptance chain from the gathered p_i(d),
 //                  q_i(d) (identical in all of them) and sums the residual
-//                  (or bonus) weights of its vocab chunk, in fp64;
+//                  (or bonus) weights of its vocab chunk, and p_n alone for
+//                  the rounding fallback, in fp64;
 //   3. rej_pick  : per sequence, locates the chunk whose running mass passes
 //                  u * total, then the token inside it (inverse CDF in token
 //                  id order).
@@ -125,41 +126,77 @@ __global__ __launch_bounds__(kThreads) void rej_stats_kernel(RejectParams p) {
 
 // Weight of token t for the final draw: residual max(0, p_n - q_n) after a
 // rejection, p_k for the bonus draw, p_n for the all-zero-residual fallback.
+// Probabilities are evaluated as 2^(x * s - m * log2 e) / z from the merged
+// row statistics (m, z) of the temperature-scaled logits.
 struct DrawRows {
   const float* a;  // AR row
   const float* q;  // diffusion row, or nullptr for a plain AR draw
-  float ma, za, mq, zq;
-  __device__ __forceinline__ float w(float xa, float xq) const {
-    const float pa = expf(xa - ma) / za;
-    if (!q) return pa;
-    const float pq = expf(xq - mq) / zq;
-    return fmaxf(0.f, pa - pq);
+  float s;         // log2(e) / T
+  float ba, ra;    // m_a * log2(e), 1 / z_a
+  float bq, rq;
+  __device__ __forceinline__ void init(const RejectParams& p, const float* arow, float2 sa, const float* qrow,
+                                       float2 sq) {
+    const float l2e = 1.4426950408889634f;
+    a = arow;
+    q = qrow;
+    s = p.inv_temp * l2e;
+    ba = sa.x * l2e;
+    ra = 1.f / sa.y;
+    bq = qrow ? sq.x * l2e : 0.f;
+    rq = qrow ? 1.f / sq.y : 0.f;
   }
+  __device__ __forceinline__ float pa(float x) const { return __builtin_amdgcn_exp2f(fmaf(x, s, -ba)) * ra; }
+  __device__ __forceinline__ float pq(float x) const { return __builtin_amdgcn_exp2f(fmaf(x, s, -bq)) * rq; }
 };
 
-// Merge the per-chunk statistics of row rr in chunk order.
-__device__ __forceinline__ float2 merge_row(const RejectParams& p, int b, int rr) {
+// Merge the per-chunk statistics of row rr across one wave: lane l takes
+// chunks l, l + 64, ... (a fixed order, so the result is deterministic).
+__device__ __forceinline__ float2 merge_row_wave(const RejectParams& p, int b, int rr, int lane) {
   const float2* st = p.row_stats + ((size_t)b * (2 * p.k + 1) + rr) * p.nchunks;
   float m = kNegInf;
-  for (int c = 0; c < p.nchunks; ++c) m = fmaxf(m, st[c].x);
+  for (int c = lane; c < p.nchunks; c += 64) m = fmaxf(m, st[c].x);
+  m = wave_max(m);
   float z = 0.f;
   if (m != kNegInf)
-    for (int c = 0; c < p.nchunks; ++c)
+    for (int c = lane; c < p.nchunks; c += 64)
       if (st[c].x != kNegInf) z += st[c].y * expf(st[c].x - m);
-  return make_float2(m, z);
+  return make_float2(m, wave_sumf(z));
+}
+
+// Inclusive prefix sum over the block in thread order (fp64); `tot` gets the
+// block total. Uses red[0..3].
+__device__ __forceinline__ double block_scan_incl(double x, double* red, double* tot) {
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double y = __shfl_up(x, o);
+    if (l >= o) x += y;
+  }
+  __syncthreads();
+  if (l == 63) red[w] = x;
+  __syncthreads();
+  double off = 0.0;
+  for (int i = 0; i < w; ++i) off += red[i];
+  *tot = ((red[0] + red[1]) + red[2]) + red[3];
+  return x + off;
 }
 
 __global__ __launch_bounds__(kThreads) void rej_resid_kernel(RejectParams p) {
   __shared__ float2 mz[2 * kMaxK + 1];
   __shared__ float rho[kMaxK];
+  __shared__ float uni[kMaxK];
   __shared__ int n_sh;
   __shared__ double redd[4];
   const int c = blockIdx.x % p.nchunks, b = blockIdx.x / p.nchunks;
   const int k = p.k, nrows = 2 * k + 1;
-  for (int rr = threadIdx.x; rr < nrows; rr += kThreads) {
-    const float2 v = merge_row(p, b, rr);
-    mz[rr] = v;
-    if (!(isfinite(v.x) && v.y > 0.f && isfinite(v.y)) && c == 0 && p.dev_status) atomicOr(p.dev_status, 8);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int rr = wave; rr < nrows; rr += kThreads / 64) {
+    const float2 v = merge_row_wave(p, b, rr, lane);
+    if (lane == 0) {
+      mz[rr] = v;
+      if (c == 0) p.row_mz[(size_t)b * nrows + rr] = v;
+      if (!(isfinite(v.x) && v.y > 0.f && isfinite(v.y)) && c == 0 && p.dev_status) atomicOr(p.dev_status, 8);
+    }
   }
   __syncthreads();
   for (int i = threadIdx.x; i < k; i += kThreads) {
@@ -174,15 +211,12 @@ __global__ __launch_bounds__(kThreads) void rej_resid_kernel(RejectParams p) {
       r = pq > 0.f ? pa / pq : INFINITY;
     }
     rho[i] = r;
+    uni[i] = p.uniforms[(size_t)b * (k + 1) + i];
   }
   __syncthreads();
   if (threadIdx.x == 0) {
     int n = 0;
-    while (n < k) {
-      const float a = fminf(1.f, rho[n]);
-      if (p.uniforms[(size_t)b * (k + 1) + n] < a) ++n;
-      else break;
-    }
+    while (n < k && uni[n] < fminf(1.f, rho[n])) ++n;
     n_sh = n;
   }
   __syncthreads();
@@ -197,133 +231,111 @@ __global__ __launch_bounds__(kThreads) void rej_resid_kernel(RejectParams p) {
     }
   }
   DrawRows dr;
-  dr.a = row_ptr(p, b, n);
-  dr.ma = mz[n].x;
-  dr.za = mz[n].y;
-  if (n < k) {
-    dr.q = row_ptr(p, b, k + 1 + n);
-    dr.mq = mz[k + 1 + n].x;
-    dr.zq = mz[k + 1 + n].y;
-  } else {
-    dr.q = nullptr;
-    dr.mq = 0.f;
-    dr.zq = 1.f;
-  }
+  dr.init(p, row_ptr(p, b, n), mz[n], n < k ? row_ptr(p, b, k + 1 + n) : nullptr,
+          n < k ? mz[k + 1 + n] : make_float2(0.f, 1.f));
+  // per chunk: mass of the draw distribution, and of p_n alone (the
+  // fallback when the residual vanishes through rounding)
   const int e0 = c * kChunk, e1 = min(e0 + kChunk, p.V);
-  double acc = 0.0;
+  float xa[kPer], xq[kPer];
+#pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const int t = e0 + threadIdx.x + kThreads * j;
-    if (t < e1) acc += (double)dr.w(dr.a[t] * p.inv_temp, dr.q ? dr.q[t] * p.inv_temp : 0.f);
+    const int t = min(e0 + threadIdx.x + kThreads * j, e1 - 1);
+    xa[j] = dr.a[t];
+    xq[j] = dr.q ? dr.q[t] : 0.f;
+  }
+  double acc = 0.0, acc_a = 0.0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    if (e0 + (int)threadIdx.x + kThreads * j < e1) {
+      const float pa = dr.pa(xa[j]);
+      const float w = dr.q ? fmaxf(0.f, pa - dr.pq(xq[j])) : pa;
+      acc += (double)w;
+      acc_a += (double)pa;
+    }
   }
   acc = block_sumd(acc, redd);
-  if (threadIdx.x == 0) p.resid_sums[(size_t)b * p.nchunks + c] = acc;
+  acc_a = block_sumd(acc_a, redd);
+  if (threadIdx.x == 0) {
+    p.resid_sums[(size_t)b * p.nchunks + c] = acc;
+    p.resid_sums[((size_t)p.B + b) * p.nchunks + c] = acc_a;
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void rej_pick_kernel(RejectParams p) {
+  __shared__ double red[4];
   __shared__ double sums[kMaxChunks];
-  __shared__ double redd[4];
-  __shared__ double scan[kThreads];
-  __shared__ int pick_c;
+  __shared__ int pick_c, last_c, first_t, last_t;
   __shared__ double pick_base;
-  __shared__ double target_sh;
-  __shared__ int first_t, last_pos;
-  const int b = blockIdx.x, k = p.k;
+  const int b = blockIdx.x, k = p.k, nrows = 2 * k + 1;
   const int n = p.decision[2 * b];
-
-  // statistics of the rows used by the draw
-  __shared__ float2 sa, sq;
-  if (threadIdx.x == 0) sa = merge_row(p, b, n);
-  if (threadIdx.x == 1 && n < k) sq = merge_row(p, b, k + 1 + n);
-  __syncthreads();
   DrawRows dr;
-  dr.a = row_ptr(p, b, n);
-  dr.ma = sa.x;
-  dr.za = sa.y;
-  if (n < k) {
-    dr.q = row_ptr(p, b, k + 1 + n);
-    dr.mq = sq.x;
-    dr.zq = sq.y;
-  } else {
+  dr.init(p, row_ptr(p, b, n), p.row_mz[(size_t)b * nrows + n], n < k ? row_ptr(p, b, k + 1 + n) : nullptr,
+          n < k ? p.row_mz[(size_t)b * nrows + k + 1 + n] : make_float2(0.f, 1.f));
+  // thread t owns chunks [cpt*t, cpt*t + cpt)
+  const int cpt = (p.nchunks + kThreads - 1) / kThreads;
+  const int c0 = cpt * threadIdx.x, c1 = min(c0 + cpt, p.nchunks);
+  double mine = 0.0;
+  for (int c = c0; c < c1; ++c) mine += (sums[c] = p.resid_sums[(size_t)b * p.nchunks + c]);
+  double total;
+  double incl = block_scan_incl(mine, red, &total);
+  if (!(total > 0.0)) {
+    // the residual vanished through rounding: draw from p_n instead
     dr.q = nullptr;
-    dr.mq = 0.f;
-    dr.zq = 1.f;
+    mine = 0.0;
+    for (int c = c0; c < c1; ++c) mine += (sums[c] = p.resid_sums[((size_t)p.B + b) * p.nchunks + c]);
+    incl = block_scan_incl(mine, red, &total);
   }
-
-  for (int c = threadIdx.x; c < p.nchunks; c += kThreads) sums[c] = p.resid_sums[(size_t)b * p.nchunks + c];
-  __syncthreads();
-  __shared__ double total_sh;
+  const double target = (double)p.uniforms[(size_t)b * (k + 1) + k] * total;
   if (threadIdx.x == 0) {
-    double t = 0.0;
-    for (int c = 0; c < p.nchunks; ++c) t += sums[c];
-    total_sh = t;
+    pick_c = 0x7fffffff;
+    last_c = -1;
+    first_t = 0x7fffffff;
+    last_t = -1;
   }
   __syncthreads();
-  if (!(total_sh > 0.0)) {
-    // residual vanished through rounding: draw from p_n instead
-    dr.q = nullptr;
-    for (int c = 0; c < p.nchunks; ++c) {
-      const int e0 = c * kChunk, e1 = min(e0 + kChunk, p.V);
-      double acc = 0.0;
-      for (int j = 0; j < kPer; ++j) {
-        const int t = e0 + threadIdx.x + kThreads * j;
-        if (t < e1) acc += (double)dr.w(dr.a[t] * p.inv_temp, 0.f);
-      }
-      acc = block_sumd(acc, redd);
-      if (threadIdx.x == 0) sums[c] = acc;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      double t = 0.0;
-      for (int c = 0; c < p.nchunks; ++c) t += sums[c];
-      total_sh = t;
-    }
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) {
-    const double target = (double)p.uniforms[(size_t)b * (k + 1) + k] * total_sh;
-    double run = 0.0;
-    int cf = -1, clast = 0;
-    double base = 0.0, base_last = 0.0;
-    for (int c = 0; c < p.nchunks; ++c) {
-      if (sums[c] > 0.0) { clast = c; base_last = run; }
-      if (cf < 0 && run + sums[c] > target) { cf = c; base = run; }
+  // first chunk whose running mass passes the target; last chunk with mass
+  // (the fallback when rounding leaves the target at the total)
+  {
+    double run = incl - mine;
+    int mf = 0x7fffffff, ml = -1;
+    for (int c = c0; c < c1; ++c) {
+      if (sums[c] > 0.0) ml = c;
+      if (mf == 0x7fffffff && run + sums[c] > target) mf = c;
       run += sums[c];
     }
-    if (cf < 0) { cf = clast; base = base_last; }
-    pick_c = cf;
-    pick_base = base;
-    target_sh = target;
-    first_t = 0x7fffffff;
-    last_pos = -1;
+    if (mf != 0x7fffffff) atomicMin(&pick_c, mf);
+    if (ml >= 0) atomicMax(&last_c, ml);
   }
   __syncthreads();
+  const int cp = pick_c != 0x7fffffff ? pick_c : max(last_c, 0);
+  if (threadIdx.x == 0) {
+    double base = 0.0;
+    for (int c = 0; c < cp; ++c) base += sums[c];
+    pick_base = base;
+  }
   // inverse CDF inside the chosen chunk: thread t owns kPer consecutive tokens
-  const int e0 = pick_c * kChunk, e1 = min(e0 + kChunk, p.V);
-  float w[kPer];
-  double mine = 0.0;
+  const int e0 = cp * kChunk, e1 = min(e0 + kChunk, p.V);
+  float w[kPer], xq[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const int t = e0 + threadIdx.x * kPer + j;
-    w[j] = t < e1 ? dr.w(dr.a[t] * p.inv_temp, dr.q ? dr.q[t] * p.inv_temp : 0.f) : 0.f;
-    mine += (double)w[j];
+    const int t = min(e0 + (int)threadIdx.x * kPer + j, e1 - 1);
+    w[j] = dr.a[t];
+    xq[j] = dr.q ? dr.q[t] : 0.f;
   }
-  scan[threadIdx.x] = mine;
-  __syncthreads();
-  if (threadIdx.x == 0) {  // exclusive scan in token order
-    double run = pick_base;
-    for (int i = 0; i < kThreads; ++i) {
-      const double x = scan[i];
-      scan[i] = run;
-      run += x;
-    }
+  double tsum = 0.0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const float pa = dr.pa(w[j]);
+    w[j] = e0 + (int)threadIdx.x * kPer + j < e1 ? (dr.q ? fmaxf(0.f, pa - dr.pq(xq[j])) : pa) : 0.f;
+    tsum += (double)w[j];
   }
-  __syncthreads();
-  double run = scan[threadIdx.x];
-  const double target = target_sh;
+  double ctot;
+  double run = block_scan_incl(tsum, red, &ctot) - tsum;  // its barriers also publish pick_base
+  run += pick_base;
   int mine_first = 0x7fffffff, mine_last = -1;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const int t = e0 + threadIdx.x * kPer + j;
+    const int t = e0 + (int)threadIdx.x * kPer + j;
     run += (double)w[j];
     if (t < e1) {
       if (run > target && mine_first == 0x7fffffff) mine_first = t;
@@ -331,9 +343,9 @@ __global__ __launch_bounds__(kThreads) void rej_pick_kernel(RejectParams p) {
     }
   }
   if (mine_first != 0x7fffffff) atomicMin(&first_t, mine_first);
-  if (mine_last >= 0) atomicMax(&last_pos, mine_last);
+  if (mine_last >= 0) atomicMax(&last_t, mine_last);
   __syncthreads();
-  if (threadIdx.x == 0) p.next_token[b] = first_t != 0x7fffffff ? first_t : max(last_pos, 0);
+  if (threadIdx.x == 0) p.next_token[b] = first_t != 0x7fffffff ? first_t : max(last_t, 0);
 }
 
 }  // namespace
@@ -342,8 +354,9 @@ size_t reject_workspace_bytes(int B, int k, int V) {
   const size_t nchunks = (size_t)(V + kChunk - 1) / kChunk;
   size_t bytes = 0;
   bytes += ((size_t)B * (2 * k + 1) * nchunks * sizeof(float2) + 255) / 256 * 256;
-  bytes += ((size_t)B * nchunks * sizeof(double) + 255) / 256 * 256;
+  bytes += ((size_t)2 * B * nchunks * sizeof(double) + 255) / 256 * 256;
   bytes += ((size_t)B * 2 * sizeof(int32_t) + 255) / 256 * 256;
+  bytes += ((size_t)B * (2 * k + 1) * sizeof(float2) + 255) / 256 * 256;
   return bytes;
 }
 

@@ -18,8 +18,11 @@ struct AttnParams {
   void* out;
   float* lse;
   int32_t* dev_status;
-  float* part_o;   // [S, B, R, Hq, D] unnormalised partial outputs (S > 1 only)
-  float* part_ml;  // [S, B, R, Hq, 2] running max (log2 domain) and sum
+  // split partials (S > 1 only): normalised output of each split over its
+  // keys, [S, B, R, Hq, D] in the input precision (bf16 or fp32), and its
+  // log-sum-exp in the log2 domain, [S, B, R, Hq] fp32 (-inf: no visible key)
+  void* part_o;
+  float* part_lse;
   int B, Hq, Hkv, D, g, R, k, num_blocks, block_len, cap, max_len;
   int S;          // number of prefix splits
   int chunk;      // prefix keys per split
@@ -69,8 +72,9 @@ struct RejectParams {
   float* ratio;
   int32_t* dev_status;
   float2* row_stats;    // [B, 2k+1, nchunks] (max, sum exp) per chunk
-  double* resid_sums;   // [B, nchunks] residual (or bonus) mass per chunk
+  double* resid_sums;   // [2, B, nchunks] mass per chunk of the draw distribution, then of p_n alone
   int32_t* decision;    // [B, 2]: accept length, source row kind
+  float2* row_mz;       // [B, 2k+1] merged (max, sum exp) of every row
 };
 size_t reject_workspace_bytes(int B, int k, int V);
 int reject_max_k();

@@ -93,7 +93,9 @@ int tidar_version(void);
  *
  * The prefix keys are split into workgroup-sized pieces that are reduced
  * separately and merged by log-sum-exp; the result does not depend on the
- * split count beyond floating-point rounding.
+ * split count beyond floating-point rounding. Each split's normalised output
+ * is held in the workspace in the input precision (bf16 or fp32), with its
+ * log-sum-exp in fp32.
  * ---------------------------------------------------------------------- */
 typedef struct {
   int32_t batch;           /* B >= 1 */
