@@ -36,10 +36,16 @@ def _hipcc() -> str:
     return exe
 
 
+# Per-file extra flags. The attention kernels run with the IEEE mode bit
+# clear: v_max_f32 then needs no quieting of its inputs (the scores never
+# hold NaN: out-of-range keys are loaded as zeros and masked to -inf).
+EXTRA_FLAGS = {"attn.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"]
-    cmd = [_hipcc(), *lang, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *lang, *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -26,17 +26,19 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <type_traits>
 
 namespace tidar {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint16_t u16;
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 128;          // packed query rows per workgroup (bf16 path)
 constexpr int kBN = 64;           // keys per tile
 constexpr float kNegInf = -INFINITY;
 
@@ -130,64 +132,56 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  // raw buffer (stride 0): loads at byte offsets >= bytes return zero
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+  // raw buffer (stride 0): loads at byte offsets >= bytes return zero. The
+  // fields go through readfirstlane so the descriptor is known to be uniform
+  // and stays in scalar registers.
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
+// LDS tile layout: 64 keys x D bf16 held as D/16 column pairs; element
+// (key r, dim d) sits at byte (d/16)*2048 + r*32 + (d%16)*2. A wave's
+// A-operand read of K (32 keys x 16 dims, 16 B per lane) then covers 1 KB of
+// contiguous LDS, and a transposing V read (8 keys x 32 dims) two contiguous
+// 256-B pieces: both free of bank conflicts with one address register. The
+// global->LDS copies write 1 KB (32 keys x one column pair) per instruction.
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
 template <int D>
-struct Cfg {
-  // K rows padded to 272 B (D=128): 16 consecutive rows start in distinct
-  // 4-bank groups, so the 128-bit A-operand reads are conflict-free.
-  static constexpr int KSTR = D + 8;
-  // V rows padded to 320 B: the four rows read together by one transposing
-  // ds_read_tr16_b64 land in disjoint 16-bank ranges.
-  static constexpr int VSTR = D + 32;
-  static constexpr int CPR = D / 8;                      // 16-byte chunks per row
-  static constexpr int LD_ITER = kBN * CPR / kThreads;   // chunks per thread per tile
-  static constexpr int KBUF = kBN * KSTR;
-  static constexpr int VBUF = kBN * VSTR;
-  static_assert(kBN * CPR % kThreads == 0, "tile does not divide");
+struct Lay {
+  static constexpr int NCP = D / 16;             // column pairs
+  static constexpr int TILE_BYTES = NCP * 2048;  // 64 keys
+  static constexpr int NLD = 2 * NCP;            // 1 KB copies per tile
 };
 
-// Global -> register -> LDS staging of K and V tiles. Buffer loads return
-// zero past the end of the valid range, so partial tiles (and prefetches past
-// the last tile) need no branches, and no invalid value can reach the MFMAs
-// (0 * NaN would poison them).
-template <int D>
-struct Stage {
-  static constexpr int ROWS_PER_IT = kThreads / Cfg<D>::CPR;  // tile rows covered per load round
-  uint4 k[Cfg<D>::LD_ITER], v[Cfg<D>::LD_ITER];
+// Global -> LDS copy of one 64-key tile (rows row0 .. row0+63 of a buffer
+// resource whose rows are row_bytes apart), without passing through
+// registers. Copy j moves column pair j/2 of keys 32*(j%2) .. +31; lane l
+// fetches 16 B of key l/2. Rows past the resource's end arrive as zeros, so
+// partial tiles need no branches and no invalid value reaches the MFMAs.
+template <int D, int WAVES>
+__device__ __forceinline__ void copy_tile(__amdgpu_buffer_rsrc_t r, uint32_t vo, int row0, uint32_t row_bytes,
+                                          lds_u8* dst, int wave) {
+#pragma unroll
+  for (int i = 0; i < Lay<D>::NLD / WAVES; ++i) {
+    const int j = wave + WAVES * i;
+    const int cp = j >> 1, h = j & 1;
+    // the scalar offset is wave-uniform by construction; readfirstlane tells the compiler so
+    const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)(row0 + 32 * h) * row_bytes + 32u * cp);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + cp * 2048 + h * 1024),
+                                             16, vo, so, 0, 0);
+  }
+}
 
-  // per-thread part of the byte offset; the row part goes in the scalar offset
-  __device__ __forceinline__ static uint32_t voff(int tid, uint32_t row_bytes) {
-    return (uint32_t)(tid / Cfg<D>::CPR) * row_bytes + (uint32_t)(tid % Cfg<D>::CPR) * 16u;
-  }
-  __device__ __forceinline__ static int lds_off(int tid, int stride) {
-    return (tid / Cfg<D>::CPR) * stride + (tid % Cfg<D>::CPR) * 8;
-  }
-  __device__ __forceinline__ void load_k(__amdgpu_buffer_rsrc_t r, uint32_t vo, int row0, uint32_t row_bytes) {
-#pragma unroll
-    for (int it = 0; it < Cfg<D>::LD_ITER; ++it)
-      k[it] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                           r, vo, (row0 + it * ROWS_PER_IT) * row_bytes, 0));
-  }
-  __device__ __forceinline__ void load_v(__amdgpu_buffer_rsrc_t r, uint32_t vo, int row0, uint32_t row_bytes) {
-#pragma unroll
-    for (int it = 0; it < Cfg<D>::LD_ITER; ++it)
-      v[it] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                           r, vo, (row0 + it * ROWS_PER_IT) * row_bytes, 0));
-  }
-  __device__ __forceinline__ void store_k(u16* ks, int lo) const {
-#pragma unroll
-    for (int it = 0; it < Cfg<D>::LD_ITER; ++it)
-      *reinterpret_cast<uint4*>(ks + lo + it * ROWS_PER_IT * Cfg<D>::KSTR) = k[it];
-  }
-  __device__ __forceinline__ void store_v(u16* vs, int lo) const {
-#pragma unroll
-    for (int it = 0; it < Cfg<D>::LD_ITER; ++it)
-      *reinterpret_cast<uint4*>(vs + lo + it * ROWS_PER_IT * Cfg<D>::VSTR) = v[it];
-  }
-};
+__device__ __forceinline__ uint32_t copy_voff(int lane, uint32_t row_bytes) {
+  return (uint32_t)(lane >> 1) * row_bytes + (uint32_t)(lane & 1) * 16u;
+}
+
+// wait for this wave's outstanding global->LDS copies
+__device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
 
 // Per-wave state: NQT tiles of 32 query rows, online softmax in the log2
 // domain. The running maximum is only raised when a tile exceeds it by more
@@ -199,36 +193,60 @@ template <int D, int NQT>
 struct Wave {
   static constexpr int DSTEPS = D / 16;
   static constexpr int DT = D / 32;
+  static constexpr int SPS = 32 / DSTEPS;  // scores per row turned into P per QK k-step
   using S = f32x16[NQT][2];
   using P = bf16x8[NQT][4];
   bf16x8 qf[NQT][DSTEPS];
   f32x16 o[NQT][DT];
   float m[NQT];  // reference maximum (log2 domain), per lane = per query row
-  float l[NQT];  // this lane's share of the running sum
+  float l[NQT];  // this lane's share of the running sum (of the bf16-rounded P)
+  uint32_t ka;   // LDS byte offset of this lane's K fragment inside a tile
+  uint32_t va;   // LDS byte offset of this lane's V^T fragment inside a tile
 
-  // S^T = K Q^T for one 64-key tile: s[nt][mt][v] is the score of key
-  // 32*mt + 8*(v/4) + 4*half + (v%4) for this lane's row of query tile nt.
-  __device__ __forceinline__ void qk(const u16* ks, int lane, S& s) const {
-    constexpr int KSTR = Cfg<D>::KSTR;
-    const int l32 = lane & 31, half = lane >> 5;
+  __device__ __forceinline__ void init_addr(int lane) {
+    const int l32 = lane & 31, half = lane >> 5, g16 = lane & 15, gbit = (lane >> 4) & 1;
+    ka = (uint32_t)(l32 * 32 + half * 16);
+    va = (uint32_t)(gbit * 2048 + (4 * half + (g16 >> 2)) * 32 + (g16 & 3) * 8);
+  }
+
+  // K fragment: keys 32*mt + l32, dims 16*st + 8*half .. +7 (A operand of S^T = K Q^T)
+  __device__ __forceinline__ bf16x8 kfrag(const lds_u8* kb, int st, int mt) const {
+    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kb + ka + st * 2048 + mt * 1024);
+  }
+  // V^T fragment for k-step ks4 (keys 16*ks4 .. +15) and dims 32*dt .. +31:
+  // two transposing reads; within each group of 16 lanes, lane j points at
+  // 4 consecutive dims of one key and lane i receives one dim of 4 keys.
+  __device__ __forceinline__ bf16x8 vfrag(const lds_u8* vb, int ks4, int dt) const {
+    const lds_u8* p = vb + va + dt * 4096 + ks4 * 512;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 256));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+
+  // S^T = K Q^T for one tile, not interleaved (first tile and step keys).
+  // s[nt][mt][v] is the score of key 32*mt + 8*(v/4) + 4*half + (v%4).
+  __device__ __forceinline__ void qk(const lds_u8* kb, S& s) const {
 #pragma unroll
     for (int nt = 0; nt < NQT; ++nt) s[nt][0] = s[nt][1] = f32x16{};
 #pragma unroll
-    for (int st = 0; st < DSTEPS; ++st) {
+    for (int st = 0; st < DSTEPS; ++st)
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + (32 * mt + l32) * KSTR + 8 * half + 16 * st);
+        const bf16x8 a = kfrag(kb, st, mt);
 #pragma unroll
         for (int nt = 0; nt < NQT; ++nt)
           s[nt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[nt][st], s[nt][mt], 0, 0, 0);
       }
-    }
   }
 
   // keys at tile positions >= nvalid, or (step keys) outside the row's region, get -inf
   template <bool REGION>
   __device__ __forceinline__ static void mask(S& s, int lane, int nvalid, int c_base, const RowRule (&rules)[NQT]) {
-    const int half = lane >> 5;
+    // The key index of score v is a compile-time offset from 4*half. The
+    // empty asm keeps the compiler from hoisting 32 such per-lane constants
+    // out of the tile loop (they would occupy 32 registers for its length).
+    int h4 = (lane >> 5) * 4;
+    asm volatile("" : "+v"(h4));
 #pragma unroll
     for (int nt = 0; nt < NQT; ++nt)
 #pragma unroll
@@ -237,27 +255,29 @@ struct Wave {
         for (int v = 0; v < 16; ++v) {
           // branch-free on purpose: a divergent element store into the
           // score vector is easy to mis-lower, a select is not
-          const int kk = 32 * mt + 8 * (v >> 2) + 4 * half + (v & 3);
+          const int kk = h4 + (32 * mt + 8 * (v >> 2) + (v & 3));
           bool ok = kk < nvalid;
           if (REGION) ok = ok & rules[nt].sees(c_base + kk);
           s[nt][mt][v] = ok ? s[nt][mt][v] : kNegInf;
         }
   }
 
-  // Row maxima of the tile; raise the reference maximum (and rescale the
-  // accumulators) only where the tile exceeds it by more than kSlack.
-  __device__ __forceinline__ void update_max(const S& s, float sl2) {
+  // in-lane maximum of 8 scores of score group g (0..3) into mx
+  __device__ __forceinline__ static void max8(const S& s, int nt, int g, float& mx) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) mx = fmaxf(mx, fmaxf(s[nt][g >> 1][8 * (g & 1) + e], s[nt][g >> 1][8 * (g & 1) + e + 1]));
+  }
+
+  // Raise the reference maximum (and rescale the accumulators) where the
+  // tile's row maximum (log2 domain, mx holds the in-lane part of the raw
+  // score maximum) exceeds it by more than kSlack.
+  __device__ __forceinline__ void update_max(float (&mx)[NQT], float sl2) {
 #pragma unroll
     for (int nt = 0; nt < NQT; ++nt) {
-      float mx = kNegInf;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[nt][mt][v]);
-      mx = half_max(mx) * sl2;
-      const bool raise = mx > m[nt] + kSlack;
+      const float t = half_max(mx[nt]) * sl2;
+      const bool raise = t > m[nt] + kSlack;
       if (__ballot(raise)) {
-        const float mnew = raise ? mx : m[nt];
+        const float mnew = raise ? t : m[nt];
         const float alpha = raise ? __builtin_amdgcn_exp2f(m[nt] - mnew) : 1.f;  // m = -inf gives 0
         m[nt] = mnew;
         l[nt] *= alpha;
@@ -267,78 +287,238 @@ struct Wave {
     }
   }
 
-  // p = 2^(s*sl2 - m), summed into l and packed (bf16, RNE) as the B operand of O^T = V^T P^T
-  __device__ __forceinline__ void probs(const S& s, float sl2, P& pb) {
+  // P for scores [i0, i0 + n) of row tile nt (n even): each pair is rounded
+  // to bf16 (nearest even), added to the row sum and stored straight into
+  // the B operand of O^T = V^T P^T.
+  __device__ __forceinline__ void probs(const S& s, int nt, int i0, int n, float muse, float sl2, P& pb) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-    for (int nt = 0; nt < NQT; ++nt) {
-      const float muse = (m[nt] == kNegInf) ? 0.f : m[nt];
-      float lsum = 0.f;
-#pragma unroll
-      for (int ks4 = 0; ks4 < 4; ++ks4) {
-        const int mt = ks4 >> 1, vb = 8 * (ks4 & 1);
-        f32x8 pv;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float pe = __builtin_amdgcn_exp2f(fmaf(s[nt][mt][vb + e], sl2, -muse));
-          pv[e] = pe;
-          lsum += pe;
-        }
-        pb[nt][ks4] = __builtin_convertvector(pv, bf16x8);
-      }
-      l[nt] += lsum;
+    for (int j = 0; j < n; j += 2) {
+      const int i = i0 + j;
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[nt][i >> 4][i & 15], sl2, -muse));
+      const float p1 = __builtin_amdgcn_exp2f(fmaf(s[nt][(i + 1) >> 4][(i + 1) & 15], sl2, -muse));
+      const f32x2 pp = {p0, p1};
+      const bf16x2 h = __builtin_convertvector(pp, bf16x2);
+      l[nt] = __builtin_amdgcn_fdot2_f32_bf16(h, one, l[nt], false);
+      pb[nt][i >> 3][i & 7] = h[0];
+      pb[nt][i >> 3][(i & 7) + 1] = h[1];
     }
   }
 
-  // O^T += V^T P^T. B-operand index 8*half + e of k-step ks4 is key
-  // 16*ks4 + 8*(e/4) + 4*half + (e%4). The V^T fragment comes from the
-  // row-major V tile through two transposing reads: within each group of
-  // 16 lanes, lane j points at 4 consecutive d of key row j/4, and lane i
-  // receives d = (its column) for 4 consecutive keys.
-  __device__ __forceinline__ void pv(const u16* vs, int lane, const P& pb) {
-    constexpr int VSTR = Cfg<D>::VSTR;
-    const int half = lane >> 5, g16 = lane & 15;
-    const u16* vb0 = vs + (4 * half + (g16 >> 2)) * VSTR + 16 * ((lane >> 4) & 1) + 4 * (g16 & 3);
+  // One tile step in a fixed instruction order:
+  //   phase A: the next tile's S^T = K Q^T MFMAs (QK) interleaved with this
+  //            tile's probabilities (from s_cur);
+  //   phase B: this tile's O^T += V^T P^T MFMAs interleaved with the row
+  //            maxima of the next tile (NEXT).
+  // Operand fragments are read LA MFMA slots ahead; sched_barrier(0) pins
+  // each slot so the LDS, matrix and vector pipes overlap.
+  static constexpr int LA = 1;
+  // There is no branch between the phases: code motion across one would undo
+  // the interleaving.
+  template <bool QK, bool NEXT>
+  __device__ __forceinline__ void step(const lds_u8* kb_next, const lds_u8* vb_cur, const S& s_cur, S& s_next,
+                                       float sl2) {
+    float muse[NQT];
 #pragma unroll
-    for (int ks4 = 0; ks4 < 4; ++ks4) {
+    for (int nt = 0; nt < NQT; ++nt) muse[nt] = (m[nt] == kNegInf) ? 0.f : m[nt];
+    P pb;
+    // ---- phase A: slot j = (k-step j/2, key half j%2) ----
+    constexpr int NA = 2 * DSTEPS;
+    bf16x8 kf[NA];
+    if (QK) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const u16* vp = vb0 + 16 * ks4 * VSTR + 32 * dt;
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vp + 8 * VSTR));
-        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      for (int nt = 0; nt < NQT; ++nt) s_next[nt][0] = s_next[nt][1] = f32x16{};
+#pragma unroll
+      for (int j = 0; j < LA; ++j) kf[j] = kfrag(kb_next, j >> 1, j & 1);
+    }
+#pragma unroll
+    for (int j = 0; j < NA; ++j) {
+      if (QK && j + LA < NA) kf[j + LA] = kfrag(kb_next, (j + LA) >> 1, (j + LA) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (QK) {
 #pragma unroll
         for (int nt = 0; nt < NQT; ++nt)
-          o[nt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[nt][ks4], o[nt][dt], 0, 0, 0);
+          s_next[nt][j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j], qf[nt][j >> 1], s_next[nt][j & 1], 0, 0, 0);
       }
+#pragma unroll
+      for (int nt = 0; nt < NQT; ++nt) probs(s_cur, nt, (SPS / 2) * j, SPS / 2, muse[nt], sl2, pb);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // ---- phase B: slot j = (k-step j/DT, dim tile j%DT) ----
+    float mx[NQT];
+#pragma unroll
+    for (int nt = 0; nt < NQT; ++nt) mx[nt] = kNegInf;
+    constexpr int NB = 4 * DT;
+    bf16x8 vf[NB];
+#pragma unroll
+    for (int j = 0; j < LA; ++j) vf[j] = vfrag(vb_cur, j / DT, j % DT);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (j + LA < NB) vf[j + LA] = vfrag(vb_cur, (j + LA) / DT, (j + LA) % DT);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int nt = 0; nt < NQT; ++nt)
+        o[nt][j % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], pb[nt][j / DT], o[nt][j % DT], 0, 0, 0);
+      if (NEXT && (j % (NB / 4)) == 0) {
+#pragma unroll
+        for (int nt = 0; nt < NQT; ++nt) max8(s_next, nt, j / (NB / 4), mx[nt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (NEXT) update_max(mx, sl2);
+  }
+
+  // max of a whole (masked) tile, then the reference maximum update
+  __device__ __forceinline__ void tile_max(const S& s, float sl2) {
+    float mx[NQT];
+#pragma unroll
+    for (int nt = 0; nt < NQT; ++nt) {
+      mx[nt] = kNegInf;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) max8(s, nt, g, mx[nt]);
+    }
+    update_max(mx, sl2);
   }
 };
 
-// Interleave the next tile's QK^T MFMAs with this tile's exponentials so the
-// matrix and vector pipes work at the same time within one wave.
-__device__ __forceinline__ void interleave_qk_softmax() {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read (K fragment)
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // six VALU
+// Where the keys of tile u of a workgroup come from: first the prefix tiles
+// (KV cache rows, row stride D), then, for the split that owns the last
+// prefix keys, the step's own keys visible to its rows (k_step / v_step
+// rows, stride Hkv*D) in at most two contiguous ranges.
+struct TileSrc {
+  const void* k;       // K rows of the range (resource base)
+  const void* v;       // V rows of the range
+  uint32_t bytes;      // resource size: rows past it load as zeros
+  int row0;            // first row of the tile in the resource
+  uint32_t row_bytes;
+  uint32_t vo;         // per-lane part of the copy offsets
+  int nvalid;          // rows of the tile that exist
+  int c_base;          // step-key index of the tile's first key (local tiles)
+  bool local;
+};
+
+struct TileSeq {
+  int np;                             // prefix tiles
+  int nl0, nl1;                       // local tiles of the two ranges
+  int nk;                             // prefix keys
+  int c_lo0, c_hi0, c_lo1, c_hi1;     // the local ranges
+  const void *pk, *pv, *lk, *lv;      // prefix and step-key bases
+  uint32_t pbytes, lbytes0, lbytes1;
+  uint32_t prb, lrb, pvo, lvo;
+  __device__ __forceinline__ int count() const { return __builtin_amdgcn_readfirstlane(np + nl0 + nl1); }
+  __device__ __forceinline__ TileSrc at(int u) const {
+    // scalar arithmetic only (no selection between fields): the struct then
+    // stays in registers
+    TileSrc t;
+    const int pre = u < np;                 // 1 for a prefix tile
+    const int sec = (u >= np + nl0);        // 1 for the second local range
+    const int loc = u - np - sec * nl0;     // tile index inside its local range
+    const int c_lo = c_lo0 + sec * (c_lo1 - c_lo0);
+    const int c_hi = c_hi0 + sec * (c_hi1 - c_hi0);
+    const int c0 = c_lo + loc * kBN;
+    // every field is wave-uniform; readfirstlane lets the compiler keep the
+    // tile loop's control flow scalar
+    t.local = !pre;
+    t.row0 = __builtin_amdgcn_readfirstlane(pre ? u * kBN : c0);
+    t.c_base = __builtin_amdgcn_readfirstlane(pre ? 0 : c0);
+    t.nvalid = __builtin_amdgcn_readfirstlane(pre ? min(kBN, nk - u * kBN) : min(kBN, c_hi - c0));
+    t.bytes = __builtin_amdgcn_readfirstlane(pre ? pbytes : (lbytes0 + (uint32_t)sec * (lbytes1 - lbytes0)));
+    t.row_bytes = __builtin_amdgcn_readfirstlane(pre ? prb : lrb);
+    t.vo = pre ? pvo : lvo;
+    t.k = pre ? pk : lk;
+    t.v = pre ? pv : lv;
+    return t;
   }
+};
+
+// Iteration t of the tile loop when tile t+1 is a full prefix tile: the
+// fully interleaved step with no other path, so the accumulators keep their
+// registers across iterations.
+template <int D, int NQT, int WAVES>
+__device__ __forceinline__ void main_iter(Wave<D, NQT>& st, lds_u8* __restrict__ kb_dst,
+                                          const lds_u8* __restrict__ kb_next, const lds_u8* __restrict__ vb_cur,
+                                          lds_u8* __restrict__ vb_dst, const TileSeq& seq, int t, int wave,
+                                          float sl2, typename Wave<D, NQT>::S& sA, typename Wave<D, NQT>::S& sB) {
+  if (t + 2 < seq.count()) {
+    const TileSrc a = seq.at(t + 2);
+    copy_tile<D, WAVES>(make_rsrc(a.k, a.bytes), a.vo, a.row0, a.row_bytes, kb_dst, wave);
+  }
+  copy_tile<D, WAVES>(make_rsrc(seq.pv, seq.pbytes), seq.pvo, (t + 1) * kBN, seq.prb, vb_dst, wave);
+  st.template step<true, true>(kb_next, vb_cur, sA, sB, sl2);
+#pragma unroll
+  for (int nt = 0; nt < NQT; ++nt) {
+    sA[nt][0] = sB[nt][0];
+    sA[nt][1] = sB[nt][1];
+  }
+  wait_copies();
 }
 
-template <int D, int NQT>
-__global__ __launch_bounds__(kThreads, NQT == 1 ? 2 : 1) void attn_bf16_kernel(AttnParams p) {
-  using C = Cfg<D>;
+// One iteration t of the tile loop: copies of K[t+2] (into kb_dst) and
+// V[t+1] (into vb_dst) are issued, then the tile step runs on K[t+1]
+// (kb_next) and V[t] (vb_cur). The four buffers are distinct; passing them as
+// restrict pointers lets the compiler see that the reads do not wait for the
+// copies in flight. A next tile that needs a mask (the partial last prefix
+// tile, or step keys under the region rule) takes the non-interleaved path.
+template <int D, int NQT, int WAVES>
+__device__ __forceinline__ void tile_iter(Wave<D, NQT>& st, lds_u8* __restrict__ kb_dst,
+                                          const lds_u8* __restrict__ kb_next, const lds_u8* __restrict__ vb_cur,
+                                          lds_u8* __restrict__ vb_dst, const TileSeq& seq, int t, int wave, int lane,
+                                          const RowRule (&rules)[NQT], float sl2, typename Wave<D, NQT>::S& sA,
+                                          typename Wave<D, NQT>::S& sB) {
   using W = Wave<D, NQT>;
-  constexpr int DSTEPS = D / 16, DT = D / 32;
-  constexpr int WROWS = 32 * NQT;       // query rows per wave
-  constexpr int BM = kWaves * WROWS;    // query rows per workgroup
-  __shared__ __attribute__((aligned(16))) u16 ks[2][C::KBUF];
-  __shared__ __attribute__((aligned(16))) u16 vs[2][C::VBUF];
+  const int ntot = seq.count();
+  if (t + 2 < ntot) {
+    const TileSrc a = seq.at(t + 2);
+    copy_tile<D, WAVES>(make_rsrc(a.k, a.bytes), a.vo, a.row0, a.row_bytes, kb_dst, wave);
+  }
+  if (t + 1 >= ntot) {
+    st.template step<false, false>(nullptr, vb_cur, sA, sB, sl2);
+  } else {
+    const TileSrc n = seq.at(t + 1);
+    copy_tile<D, WAVES>(make_rsrc(n.v, n.bytes), n.vo, n.row0, n.row_bytes, vb_dst, wave);
+    if (n.local || n.nvalid < kBN) {
+      st.qk(kb_next, sB);
+      if (n.local)
+        W::template mask<true>(sB, lane, n.nvalid, n.c_base, rules);
+      else
+        W::template mask<false>(sB, lane, n.nvalid, 0, rules);
+      st.template step<false, false>(nullptr, vb_cur, sA, sB, sl2);
+      st.tile_max(sB, sl2);
+    } else {
+      st.template step<true, true>(kb_next, vb_cur, sA, sB, sl2);
+    }
+#pragma unroll
+    for (int nt = 0; nt < NQT; ++nt) {
+      sA[nt][0] = sB[nt][0];
+      sA[nt][1] = sB[nt][1];
+    }
+  }
+  wait_copies();
+}
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+template <int D, int NQT, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kernel(AttnParams p) {
+  using W = Wave<D, NQT>;
+  using L = Lay<D>;
+  constexpr int DSTEPS = D / 16, DT = D / 32;
+  constexpr int WROWS = 32 * NQT;      // query rows per wave
+  constexpr int BM = WAVES * WROWS;    // query rows per workgroup
+  __shared__ __attribute__((aligned(1024))) uint8_t kb0[L::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t kb1[L::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb0[L::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb1[L::TILE_BYTES];
+  lds_u8* const KB[2] = {(lds_u8*)kb0, (lds_u8*)kb1};
+  lds_u8* const VB[2] = {(lds_u8*)vb0, (lds_u8*)vb1};
+
+  // Work-item and workgroup ids come from the intrinsics (this file is built
+  // with the IEEE mode bit clear, which keeps the device-library accessors
+  // behind threadIdx/blockIdx from being inlined, and a call would hide that
+  // the workgroup id is uniform).
+  const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
 
-  int w = remap_xcd(blockIdx.x, gridDim.x);
+  int w = remap_xcd((int)__builtin_amdgcn_workgroup_id_x(), p.B * p.Hkv * p.qtiles * p.S);
   const int qt = w % p.qtiles;
   w /= p.qtiles;
   const int s = w % p.S;
@@ -346,7 +526,7 @@ __global__ __launch_bounds__(kThreads, NQT == 1 ? 2 : 1) void attn_bf16_kernel(A
   const int kvh = w % p.Hkv;
   const int b = w / p.Hkv;
 
-  int len = p.cache_len[b];
+  int len = __builtin_amdgcn_readfirstlane(p.cache_len[b]);  // uniform: keeps the tile loop scalar
   if (len < 0 || len > p.max_len) {
     if (tid == 0 && p.dev_status) atomicOr(p.dev_status, 1);
     len = min(max(len, 0), p.max_len);
@@ -358,6 +538,7 @@ __global__ __launch_bounds__(kThreads, NQT == 1 ? 2 : 1) void attn_bf16_kernel(A
 
   const int M = p.R * p.g;
   W st;
+  st.init_addr(lane);
   RowRule rules[NQT];
 #pragma unroll
   for (int nt = 0; nt < NQT; ++nt) {
@@ -377,89 +558,85 @@ __global__ __launch_bounds__(kThreads, NQT == 1 ? 2 : 1) void attn_bf16_kernel(A
   }
   const float sl2 = p.scale_log2;
 
-  // ---- prefix keys [kbeg, kend) ----
-  // Software pipeline over 64-key tiles, one barrier per tile. At the top of
-  // iteration t the scores of tile t are in registers, K[t+1] is in
-  // ks[(t+1)&1] and V[t] in vs[t&1]; the loads of K[t+2] and V[t+1] are in
-  // flight while the wave computes QK^T(t+1), softmax(t) and PV(t).
+  // ---- the tile sequence: prefix keys [kbeg, kend), then (last split only)
+  // the step's own keys under the region rule ----
+  TileSeq seq;
+  seq.nk = __builtin_amdgcn_readfirstlane(nk);
+  seq.np = __builtin_amdgcn_readfirstlane((nk + kBN - 1) / kBN);
+  seq.prb = D * 2;
+  seq.pvo = copy_voff(lane, seq.prb);
   const size_t head_off = (size_t)(b * p.Hkv + kvh) * p.cap * D + (size_t)kbeg * D;
-  const __amdgpu_buffer_rsrc_t kr = make_rsrc(reinterpret_cast<const u16*>(p.k_cache) + head_off, (uint32_t)nk * D * 2);
-  const __amdgpu_buffer_rsrc_t vr = make_rsrc(reinterpret_cast<const u16*>(p.v_cache) + head_off, (uint32_t)nk * D * 2);
-  const int ntile = (nk + kBN - 1) / kBN;
-  const uint32_t rb = D * 2;
-  const uint32_t vo = Stage<D>::voff(tid, rb);
-  const int klo = Stage<D>::lds_off(tid, C::KSTR), vlo = Stage<D>::lds_off(tid, C::VSTR);
-  Stage<D> stg;
-  typename W::S s_cur, s_next;
-  typename W::P pb;
-  if (ntile > 0) {
-    stg.load_k(kr, vo, 0, rb);
-    stg.load_v(vr, vo, 0, rb);
-    stg.store_k(ks[0], klo);
-    stg.store_v(vs[0], vlo);
-    stg.load_k(kr, vo, kBN, rb);
-    stg.store_k(ks[1], klo);
-    __syncthreads();
-    st.qk(ks[0], lane, s_cur);
-  }
-  for (int t = 0; t < ntile; ++t) {
-    // all reads of ks[t&1] (QK^T of tile t, issued in the previous iteration
-    // or the prologue) and of vs[(t+1)&1] (PV of tile t-1) are done before
-    // this iteration overwrites them
-    __syncthreads();
-    stg.load_k(kr, vo, (t + 2) * kBN, rb);
-    stg.load_v(vr, vo, (t + 1) * kBN, rb);
-    const int nvalid = nk - t * kBN;
-    if (nvalid < kBN) W::template mask<false>(s_cur, lane, nvalid, 0, rules);
-    st.update_max(s_cur, sl2);
-    if (t + 1 < ntile) {
-      st.qk(ks[(t + 1) & 1], lane, s_next);
-      st.probs(s_cur, sl2, pb);
-      interleave_qk_softmax();
-    } else {
-      st.probs(s_cur, sl2, pb);
-    }
-    st.pv(vs[t & 1], lane, pb);
-    stg.store_k(ks[t & 1], klo);
-    stg.store_v(vs[(t + 1) & 1], vlo);
-#pragma unroll
-    for (int nt = 0; nt < NQT; ++nt) {
-      s_cur[nt][0] = s_next[nt][0];
-      s_cur[nt][1] = s_next[nt][1];
-    }
-  }
-  __syncthreads();
-
-  // ---- the step's own keys under the region rule (last split only) ----
+  seq.pk = reinterpret_cast<const u16*>(p.k_cache) + head_off;
+  seq.pv = reinterpret_cast<const u16*>(p.v_cache) + head_off;
+  seq.pbytes = (uint32_t)nk * seq.prb;
+  seq.nl0 = seq.nl1 = 0;
+  seq.c_lo0 = seq.c_hi0 = seq.c_lo1 = seq.c_hi1 = 0;
+  seq.lrb = (uint32_t)p.Hkv * D * 2;
+  seq.lvo = copy_voff(lane, seq.lrb);
+  const size_t step_off = ((size_t)b * p.R * p.Hkv + kvh) * D;
+  seq.lk = reinterpret_cast<const u16*>(p.k_step) + step_off;
+  seq.lv = reinterpret_cast<const u16*>(p.v_step) + step_off;
+  seq.lbytes0 = seq.lbytes1 = 0;
   if (last) {
     const int m_lo = qt * BM;
     const int m_hi = min(M, m_lo + BM) - 1;
     const LocalRanges lr = local_ranges(m_lo / p.g, m_hi / p.g, p.k, p.block_len);
-    const uint32_t row_bytes = (uint32_t)p.Hkv * D * 2;
-    const size_t step_off = ((size_t)b * p.R * p.Hkv + kvh) * D;
-    const u16* kst = reinterpret_cast<const u16*>(p.k_step) + step_off;
-    const u16* vst = reinterpret_cast<const u16*>(p.v_step) + step_off;
-    for (int seg = 0; seg < lr.n; ++seg) {
-      const int c_lo = seg == 0 ? lr.a0 : lr.b0;
-      const int c_hi = seg == 0 ? lr.a1 : lr.b1;
-      const uint32_t bytes = (uint32_t)(c_hi - 1) * row_bytes + D * 2;  // rows < c_hi are valid
-      const __amdgpu_buffer_rsrc_t lkr = make_rsrc(kst, bytes);
-      const __amdgpu_buffer_rsrc_t lvr = make_rsrc(vst, bytes);
-      const uint32_t lvo = Stage<D>::voff(tid, row_bytes);
-      for (int c0 = c_lo; c0 < c_hi; c0 += kBN) {
-        stg.load_k(lkr, lvo, c0, row_bytes);
-        stg.load_v(lvr, lvo, c0, row_bytes);
-        stg.store_k(ks[0], klo);
-        stg.store_v(vs[0], vlo);
-        __syncthreads();
-        st.qk(ks[0], lane, s_cur);
-        W::template mask<true>(s_cur, lane, min(kBN, c_hi - c0), c0, rules);
-        st.update_max(s_cur, sl2);
-        st.probs(s_cur, sl2, pb);
-        st.pv(vs[0], lane, pb);
-        __syncthreads();
-      }
+    // uniform by construction; readfirstlane keeps the tile loop scalar
+    const int n = __builtin_amdgcn_readfirstlane(lr.n);
+    if (n > 0) {
+      seq.c_lo0 = __builtin_amdgcn_readfirstlane(lr.a0);
+      seq.c_hi0 = __builtin_amdgcn_readfirstlane(lr.a1);
+      seq.nl0 = __builtin_amdgcn_readfirstlane((seq.c_hi0 - seq.c_lo0 + kBN - 1) / kBN);
+      seq.lbytes0 = (uint32_t)(seq.c_hi0 - 1) * seq.lrb + D * 2;  // rows < c_hi are valid
     }
+    if (n > 1) {
+      seq.c_lo1 = __builtin_amdgcn_readfirstlane(lr.b0);
+      seq.c_hi1 = __builtin_amdgcn_readfirstlane(lr.b1);
+      seq.nl1 = __builtin_amdgcn_readfirstlane((seq.c_hi1 - seq.c_lo1 + kBN - 1) / kBN);
+      seq.lbytes1 = (uint32_t)(seq.c_hi1 - 1) * seq.lrb + D * 2;
+    }
+  }
+  const int ntot = __builtin_amdgcn_readfirstlane(seq.count());
+
+  // Software pipeline over 64-key tiles, one barrier per tile. At the top of
+  // iteration t the scores of tile t are in registers (masked, with the
+  // reference maximum already raised for them), K[t+1] is in KB[(t+1)&1]
+  // and V[t] in VB[t&1]; the copies of K[t+2] and V[t+1] fly while the wave
+  // computes QK^T(t+1), P(t) and PV(t).
+  typename W::S sA, sB;
+  if (ntot > 0) {
+    const TileSrc t0 = seq.at(0);
+    copy_tile<D, WAVES>(make_rsrc(t0.k, t0.bytes), t0.vo, t0.row0, t0.row_bytes, KB[0], wave);
+    copy_tile<D, WAVES>(make_rsrc(t0.v, t0.bytes), t0.vo, t0.row0, t0.row_bytes, VB[0], wave);
+    if (ntot > 1) {
+      const TileSrc t1 = seq.at(1);
+      copy_tile<D, WAVES>(make_rsrc(t1.k, t1.bytes), t1.vo, t1.row0, t1.row_bytes, KB[1], wave);
+    }
+    wait_copies();
+    __syncthreads();
+    st.qk(KB[0], sA);
+    if (t0.local)
+      W::template mask<true>(sA, lane, t0.nvalid, t0.c_base, rules);
+    else if (t0.nvalid < kBN)
+      W::template mask<false>(sA, lane, t0.nvalid, 0, rules);
+    st.tile_max(sA, sl2);
+  }
+  // iterations whose next tile is a full prefix tile run a loop of their own
+  const int tmain = __builtin_amdgcn_readfirstlane(max(0, min(nk / kBN, ntot) - 1));
+  int t = 0;
+  for (; t < tmain; ++t) {
+    const int par = t & 1;
+    // all reads of K[t] (QK^T of tile t) and V[t-1] (PV of tile t-1) are
+    // done before this iteration's copies overwrite their buffers
+    __syncthreads();
+    main_iter<D, NQT, WAVES>(st, par ? KB[1] : KB[0], par ? KB[0] : KB[1], par ? VB[1] : VB[0],
+                             par ? VB[0] : VB[1], seq, t, wave, sl2, sA, sB);
+  }
+  for (; t < ntot; ++t) {
+    const int par = t & 1;
+    __syncthreads();
+    tile_iter<D, NQT, WAVES>(st, par ? KB[1] : KB[0], par ? KB[0] : KB[1], par ? VB[1] : VB[0],
+                             par ? VB[0] : VB[1], seq, t, wave, lane, rules, sl2, sA, sB);
   }
 
   // o[nt][dt][v] holds O^T[d = 32*dt + 8*(v/4) + 4*half + v%4][this lane's row]
@@ -471,41 +648,29 @@ __global__ __launch_bounds__(kThreads, NQT == 1 ? 2 : 1) void attn_bf16_kernel(A
     const int r = m / p.g;
     const int h = kvh * p.g + (m - r * p.g);
     const size_t orow = ((size_t)(b * p.R + r) * p.Hq + h);
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    u16* op;
     if (p.S == 1) {
-      const float inv = 1.f / ltot;
-      u16* op = reinterpret_cast<u16*>(p.out) + orow * D;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d = 32 * dt + 8 * i + 4 * half;
-          ushort4 pk;
-          pk.x = f32_to_bf16_bits(st.o[nt][dt][4 * i + 0] * inv);
-          pk.y = f32_to_bf16_bits(st.o[nt][dt][4 * i + 1] * inv);
-          pk.z = f32_to_bf16_bits(st.o[nt][dt][4 * i + 2] * inv);
-          pk.w = f32_to_bf16_bits(st.o[nt][dt][4 * i + 3] * inv);
-          *reinterpret_cast<ushort4*>(op + d) = pk;
-        }
+      op = reinterpret_cast<u16*>(p.out) + orow * D;
       if (p.lse && half == 0) p.lse[orow] = (st.m[nt] + log2f(ltot)) * 0.69314718055994531f;
     } else {
       // normalised partial in bf16 plus its log2-domain log-sum-exp
       const size_t prow = (size_t)s * p.B * p.R * p.Hq + orow;
-      const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-      u16* po = reinterpret_cast<u16*>(p.part_o) + prow * D;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d = 32 * dt + 8 * i + 4 * half;
-          ushort4 pk;
-          pk.x = f32_to_bf16_bits(st.o[nt][dt][4 * i + 0] * inv);
-          pk.y = f32_to_bf16_bits(st.o[nt][dt][4 * i + 1] * inv);
-          pk.z = f32_to_bf16_bits(st.o[nt][dt][4 * i + 2] * inv);
-          pk.w = f32_to_bf16_bits(st.o[nt][dt][4 * i + 3] * inv);
-          *reinterpret_cast<ushort4*>(po + d) = pk;
-        }
+      op = reinterpret_cast<u16*>(p.part_o) + prow * D;
       if (half == 0) p.part_lse[prow] = ltot > 0.f ? st.m[nt] + log2f(ltot) : kNegInf;
     }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = 32 * dt + 8 * i + 4 * half;
+        ushort4 pk;
+        pk.x = f32_to_bf16_bits(st.o[nt][dt][4 * i + 0] * inv);
+        pk.y = f32_to_bf16_bits(st.o[nt][dt][4 * i + 1] * inv);
+        pk.z = f32_to_bf16_bits(st.o[nt][dt][4 * i + 2] * inv);
+        pk.w = f32_to_bf16_bits(st.o[nt][dt][4 * i + 3] * inv);
+        *reinterpret_cast<ushort4*>(op + d) = pk;
+      }
   }
 }
 
@@ -529,9 +694,9 @@ constexpr int kF32MaxD = 256;
 __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p) {
   __shared__ float qs[kF32MaxD];
   __shared__ float ps[64];
-  const int lane = threadIdx.x;
+  const int lane = (int)__builtin_amdgcn_workitem_id_x();
   const int D = p.D;
-  int w = blockIdx.x;
+  int w = (int)__builtin_amdgcn_workgroup_id_x();
   const int M = p.R * p.g;
   const int m = w % M;
   w /= M;
@@ -643,7 +808,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   const int D = p.D;
   const int tpr = D / VEC;  // threads per row
   const size_t rows = (size_t)p.B * p.R * p.Hq;
-  const size_t gid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t gid = (size_t)__builtin_amdgcn_workgroup_id_x() * 256 + __builtin_amdgcn_workitem_id_x();
   const size_t row = gid / tpr;
   const int d = (int)(gid % tpr) * VEC;
   if (row >= rows) return;
@@ -711,7 +876,7 @@ AttnPlan plan_attn(int dtype, int B, int Hq, int Hkv, int D, int R, int max_len,
     // 32 or 64 query rows per wave; TIDAR_ATTN_WAVE_ROWS overrides the choice (tuning knob)
     pl.nqt = 1;
     if (const char* e = getenv("TIDAR_ATTN_WAVE_ROWS")) pl.nqt = atoi(e) >= 64 ? 2 : 1;
-    pl.bm = kWaves * 32 * pl.nqt;
+    pl.bm = kBM;
     pl.qtiles = (int)((M + pl.bm - 1) / pl.bm);
     base = (long)B * Hkv * pl.qtiles;
   } else {
@@ -747,14 +912,15 @@ AttnPlan plan_attn(int dtype, int B, int Hq, int Hkv, int D, int R, int max_len,
 
 hipError_t launch_attn_bf16(const AttnParams& p, hipStream_t stream) {
   const unsigned grid = (unsigned)((size_t)p.B * p.Hkv * p.qtiles * p.S);
+  // 128 query rows per workgroup: four waves of 32 rows, or two of 64
   if (p.D == 128 && p.nqt == 1)
-    hipLaunchKernelGGL((attn_bf16_kernel<128, 1>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((attn_bf16_kernel<128, 1, 4>), dim3(grid), dim3(256), 0, stream, p);
   else if (p.D == 128 && p.nqt == 2)
-    hipLaunchKernelGGL((attn_bf16_kernel<128, 2>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((attn_bf16_kernel<128, 2, 2>), dim3(grid), dim3(128), 0, stream, p);
   else if (p.D == 64 && p.nqt == 1)
-    hipLaunchKernelGGL((attn_bf16_kernel<64, 1>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((attn_bf16_kernel<64, 1, 4>), dim3(grid), dim3(256), 0, stream, p);
   else if (p.D == 64 && p.nqt == 2)
-    hipLaunchKernelGGL((attn_bf16_kernel<64, 2>), dim3(grid), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((attn_bf16_kernel<64, 2, 2>), dim3(grid), dim3(128), 0, stream, p);
   else
     return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();

@@ -82,3 +82,18 @@ class DecodeStep:
             self.attention(layer, stream)
         self.verify(stream)
         self.commit(stream)
+
+    def capture(self, fn=None):
+        """Record fn (default: run) into a HIP graph and return it.
+
+        The library calls only launch kernels on the given stream (no
+        allocation, memset or synchronisation), so the whole step can be
+        replayed with one launch from the host: g.replay().
+        """
+        fn = self.run if fn is None else fn
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g

@@ -1,7 +1,10 @@
 """GPU parity of tidar_attn_step against the fp64 oracle.
 
 Tolerances: max-abs 1e-5 for fp32 inputs and 2e-2 for bf16 inputs, on the
-stored output; LSE within 1e-4 (it never passes through bf16).
+stored output. LSE: 1e-5 for fp32; for bf16 the row sum is accumulated from
+the bf16-rounded probabilities that also feed the P.V product, each within a
+relative 2^-8 (half a bf16 ulp) of its exact value, so the log of the sum
+is within 2^-8.
 """
 import numpy as np
 import pytest
@@ -14,6 +17,7 @@ from tests.gpu_util import run_attn, oracle_inputs
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-5, "bf16": 2e-2}
+LSE_TOL = {"f32": 1e-5, "bf16": 2.0 ** -8}
 
 
 def _oracle_full(case, layer=0, cache_len=None):
@@ -43,7 +47,7 @@ def test_config2_bf16(seed):
     out, lse = run_attn(c)
     ref, rlse = _oracle_full(c)
     assert _report(f"cfg2 bf16 seed={seed}", out, ref, TOL["bf16"]) <= TOL["bf16"]
-    assert np.abs(lse - rlse).max() <= 1e-4
+    assert np.abs(lse - rlse).max() <= LSE_TOL["bf16"]
 
 
 SMALL = [
@@ -71,7 +75,7 @@ def test_small_shapes(shape, dtype, splits):
     ref, rlse = _oracle_full(c)
     assert np.isfinite(out).all()
     assert _report(f"small {shape} {dtype} S={splits}", out, ref, TOL[dtype]) <= TOL[dtype]
-    assert np.abs(lse - rlse).max() <= 1e-4
+    assert np.abs(lse - rlse).max() <= LSE_TOL[dtype]
 
 
 def _sample_rows(case, n, seed):
@@ -103,7 +107,7 @@ def test_config3_full_depth_sampled():
             got = np.stack([out[b, r, h] for b, r, h in rows])
             glse = np.array([lse[b, r, h] for b, r, h in rows])
             worst = max(worst, np.abs(got - ref).max())
-            assert np.abs(glse - rlse).max() <= 1e-4
+            assert np.abs(glse - rlse).max() <= LSE_TOL["bf16"]
     print(f"[parity] cfg3 36 layers sampled: max-abs {worst:.3e}", flush=True)
     assert worst <= TOL["bf16"]
     del rng
