@@ -805,6 +805,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p) {
 template <bool BF16>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   constexpr int VEC = BF16 ? 8 : 4;
+  constexpr int CH = 8;  // splits whose loads are in flight together
   const int D = p.D;
   const int tpr = D / VEC;  // threads per row
   const size_t rows = (size_t)p.B * p.R * p.Hq;
@@ -812,32 +813,50 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
   const size_t row = gid / tpr;
   const int d = (int)(gid % tpr) * VEC;
   if (row >= rows) return;
-  float emax = kNegInf;
-  for (int s = 0; s < p.S; ++s) emax = fmaxf(emax, p.part_lse[(size_t)s * rows + row]);
-  const float euse = (emax == kNegInf) ? 0.f : emax;
-  float wsum = 0.f;
+  // running merge (reference emax, weight sum, weighted sum), CH splits at a time
+  float emax = kNegInf, wsum = 0.f;
   float acc[VEC];
 #pragma unroll
   for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
-#pragma unroll 4
-  for (int s = 0; s < p.S; ++s) {
-    const size_t prow = (size_t)s * rows + row;
-    const float wgt = __builtin_amdgcn_exp2f(p.part_lse[prow] - euse);  // 0 for an empty split
-    wsum += wgt;
-    if (BF16) {
-      const uint4 raw = *reinterpret_cast<const uint4*>(reinterpret_cast<const u16*>(p.part_o) + prow * D + d);
-      const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+  for (int s0 = 0; s0 < p.S; s0 += CH) {
+    float e[CH];
+    float x[CH][VEC];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = fmaf(__uint_as_float(w4[i] << 16), wgt, acc[2 * i]);
-        acc[2 * i + 1] = fmaf(__uint_as_float(w4[i] & 0xffff0000u), wgt, acc[2 * i + 1]);
+    for (int j = 0; j < CH; ++j) {
+      const bool in = s0 + j < p.S;
+      const size_t prow = (size_t)(in ? s0 + j : s0) * rows + row;
+      e[j] = in ? p.part_lse[prow] : kNegInf;
+      if (BF16) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(reinterpret_cast<const u16*>(p.part_o) + prow * D + d);
+        const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[j][2 * i] = __uint_as_float(w4[i] << 16);
+          x[j][2 * i + 1] = __uint_as_float(w4[i] & 0xffff0000u);
+        }
+      } else {
+        const float4 o = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.part_o) + prow * D + d);
+        x[j][0] = o.x;
+        x[j][1] = o.y;
+        x[j][2] = o.z;
+        x[j][VEC - 1] = o.w;
       }
-    } else {
-      const float4 o = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.part_o) + prow * D + d);
-      acc[0] = fmaf(o.x, wgt, acc[0]);
-      acc[1] = fmaf(o.y, wgt, acc[1]);
-      acc[2] = fmaf(o.z, wgt, acc[2]);
-      acc[VEC - 1] = fmaf(o.w, wgt, acc[VEC - 1]);
+    }
+    float cmax = emax;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) cmax = fmaxf(cmax, e[j]);
+    if (cmax == kNegInf) continue;  // nothing visible yet
+    const float alpha = __builtin_amdgcn_exp2f(emax - cmax);  // 0 when emax = -inf
+    wsum *= alpha;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc[i] *= alpha;
+    emax = cmax;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const float wgt = __builtin_amdgcn_exp2f(e[j] - cmax);  // 0 for an empty or absent split
+      wsum += wgt;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) acc[i] = fmaf(x[j][i], wgt, acc[i]);
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;

@@ -29,6 +29,7 @@ constexpr int kChunk = 4096;            // vocab elements per chunk = 16 per thr
 constexpr int kPer = kChunk / kThreads;
 constexpr int kMaxK = 128;
 constexpr int kMaxChunks = 1024;
+constexpr int kStage = 4096;            // (row, chunk) statistics staged in LDS per sequence
 constexpr float kNegInf = -INFINITY;
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -163,6 +164,18 @@ __device__ __forceinline__ float2 merge_row_wave(const RejectParams& p, int b, i
   return make_float2(m, wave_sumf(z));
 }
 
+// The same merge from statistics staged in LDS.
+__device__ __forceinline__ float2 merge_row_lds(const float2* st, int nchunks, int lane) {
+  float m = kNegInf;
+  for (int c = lane; c < nchunks; c += 64) m = fmaxf(m, st[c].x);
+  m = wave_max(m);
+  float z = 0.f;
+  if (m != kNegInf)
+    for (int c = lane; c < nchunks; c += 64)
+      if (st[c].x != kNegInf) z += st[c].y * expf(st[c].x - m);
+  return make_float2(m, wave_sumf(z));
+}
+
 // Inclusive prefix sum over the block in thread order (fp64); `tot` gets the
 // block total. Uses red[0..3].
 __device__ __forceinline__ double block_scan_incl(double x, double* red, double* tot) {
@@ -183,6 +196,7 @@ __device__ __forceinline__ double block_scan_incl(double x, double* red, double*
 
 __global__ __launch_bounds__(kThreads) void rej_resid_kernel(RejectParams p) {
   __shared__ float2 mz[2 * kMaxK + 1];
+  __shared__ float2 st_lds[kStage];
   __shared__ float rho[kMaxK];
   __shared__ float uni[kMaxK];
   __shared__ int n_sh;
@@ -190,8 +204,40 @@ __global__ __launch_bounds__(kThreads) void rej_resid_kernel(RejectParams p) {
   const int c = blockIdx.x % p.nchunks, b = blockIdx.x / p.nchunks;
   const int k = p.k, nrows = 2 * k + 1;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the draft tokens' logits are gathered first so their latency overlaps
+  // the statistics merge
+  const int i = threadIdx.x;
+  int d = -1;
+  float da = 0.f, dq = 0.f;  // logits of draft i under the AR and diffusion rows
+  if (i < k) {
+    d = p.drafts[(size_t)b * k + i];
+    uni[i] = p.uniforms[(size_t)b * (k + 1) + i];
+    if (d >= 0 && d < p.V) {
+      da = row_ptr(p, b, i)[d];
+      dq = row_ptr(p, b, k + 1 + i)[d];
+    }
+  }
+  // per-row statistics: stage every (row, chunk) pair of this sequence in
+  // LDS with one round of loads, then merge each row across one wave
+  const int total = nrows * p.nchunks;
+  if (total <= kStage) {
+    const float2* g = p.row_stats + (size_t)b * total;
+    float2 v[kStage / kThreads];
+#pragma unroll
+    for (int j = 0; j < kStage / kThreads; ++j) {
+      const int t = threadIdx.x + kThreads * j;
+      if (t < total) v[j] = g[t];
+    }
+#pragma unroll
+    for (int j = 0; j < kStage / kThreads; ++j) {
+      const int t = threadIdx.x + kThreads * j;
+      if (t < total) st_lds[t] = v[j];
+    }
+    __syncthreads();
+  }
   for (int rr = wave; rr < nrows; rr += kThreads / 64) {
-    const float2 v = merge_row_wave(p, b, rr, lane);
+    const float2 v = total <= kStage ? merge_row_lds(st_lds + rr * p.nchunks, p.nchunks, lane)
+                                     : merge_row_wave(p, b, rr, lane);
     if (lane == 0) {
       mz[rr] = v;
       if (c == 0) p.row_mz[(size_t)b * nrows + rr] = v;
@@ -199,19 +245,17 @@ __global__ __launch_bounds__(kThreads) void rej_resid_kernel(RejectParams p) {
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < k; i += kThreads) {
-    int d = p.drafts[(size_t)b * k + i];
+  if (i < k) {
     float r = 0.f;
     if (d < 0 || d >= p.V) {
       if (c == 0 && p.dev_status) atomicOr(p.dev_status, 16);
     } else {
       const float2 sa = mz[i], sq = mz[k + 1 + i];
-      const float pa = expf(row_ptr(p, b, i)[d] * p.inv_temp - sa.x) / sa.y;
-      const float pq = expf(row_ptr(p, b, k + 1 + i)[d] * p.inv_temp - sq.x) / sq.y;
+      const float pa = expf(da * p.inv_temp - sa.x) / sa.y;
+      const float pq = expf(dq * p.inv_temp - sq.x) / sq.y;
       r = pq > 0.f ? pa / pq : INFINITY;
     }
     rho[i] = r;
-    uni[i] = p.uniforms[(size_t)b * (k + 1) + i];
   }
   __syncthreads();
   if (threadIdx.x == 0) {
