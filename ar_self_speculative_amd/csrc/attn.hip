@@ -142,18 +142,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
-// LDS tile layout: 64 keys x D bf16 held as D/16 column pairs; element
-// (key r, dim d) sits at byte (d/16)*2048 + r*32 + (d%16)*2. A wave's
-// A-operand read of K (32 keys x 16 dims, 16 B per lane) then covers 1 KB of
-// contiguous LDS, and a transposing V read (8 keys x 32 dims) two contiguous
-// 256-B pieces: both free of bank conflicts with one address register. The
+// LDS tile layout: 64 keys x D bf16 held as D/16 column pairs of 32 B per
+// key. Element (key r, dim d) sits at byte
+//   (d/16)*kCPS + r*32 + (((d%16)/8) ^ ((r/8)%2))*16 + (d%8)*2,
+// i.e. the two 16-B halves of a key's slot swap places every 8 keys, and
+// column pairs are kCPS = 2048 + 128 bytes apart. Then
+//  * a wave's A-operand read of K (32 keys x 16 dims, 16 B per lane) touches
+//    all 64 banks once per 16 lanes (the swap moves keys 8..15 of each group
+//    of 16 onto the other half of the banks), and
+//  * a transposing V read (8 keys x 32 dims, two column pairs) puts its two
+//    column pairs 128 B apart in bank space,
+// so neither conflicts, with one or two address registers per lane. The
 // global->LDS copies write 1 KB (32 keys x one column pair) per instruction.
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+constexpr int kCPS = 2048 + 128;  // bytes per column pair in LDS
 
 template <int D>
 struct Lay {
   static constexpr int NCP = D / 16;             // column pairs
-  static constexpr int TILE_BYTES = NCP * 2048;  // 64 keys
+  static constexpr int TILE_BYTES = NCP * kCPS;  // 64 keys
   static constexpr int NLD = 2 * NCP;            // 1 KB copies per tile
 };
 
@@ -171,13 +179,15 @@ __device__ __forceinline__ void copy_tile(__amdgpu_buffer_rsrc_t r, uint32_t vo,
     const int cp = j >> 1, h = j & 1;
     // the scalar offset is wave-uniform by construction; readfirstlane tells the compiler so
     const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)(row0 + 32 * h) * row_bytes + 32u * cp);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + cp * 2048 + h * 1024),
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + cp * kCPS + h * 1024),
                                              16, vo, so, 0, 0);
   }
 }
 
+// Lane l of a copy lands on LDS slot half (l%2) of key l/2; it fetches the
+// logical half that the swap puts there.
 __device__ __forceinline__ uint32_t copy_voff(int lane, uint32_t row_bytes) {
-  return (uint32_t)(lane >> 1) * row_bytes + (uint32_t)(lane & 1) * 16u;
+  return (uint32_t)(lane >> 1) * row_bytes + (uint32_t)((lane & 1) ^ ((lane >> 4) & 1)) * 16u;
 }
 
 // wait for this wave's outstanding global->LDS copies
@@ -200,26 +210,28 @@ struct Wave {
   f32x16 o[NQT][DT];
   float m[NQT];  // reference maximum (log2 domain), per lane = per query row
   float l[NQT];  // this lane's share of the running sum (of the bf16-rounded P)
-  uint32_t ka;   // LDS byte offset of this lane's K fragment inside a tile
-  uint32_t va;   // LDS byte offset of this lane's V^T fragment inside a tile
+  uint32_t ka;        // LDS byte offset of this lane's K fragment inside a tile
+  uint32_t va0, va1;  // ... of its V^T fragment, keys 0..7 and 8..15 of a k-step
 
   __device__ __forceinline__ void init_addr(int lane) {
     const int l32 = lane & 31, half = lane >> 5, g16 = lane & 15, gbit = (lane >> 4) & 1;
-    ka = (uint32_t)(l32 * 32 + half * 16);
-    va = (uint32_t)(gbit * 2048 + (4 * half + (g16 >> 2)) * 32 + (g16 & 3) * 8);
+    ka = (uint32_t)(l32 * 32 + (half ^ ((l32 >> 3) & 1)) * 16);
+    const int row = 4 * half + (g16 >> 2), lhalf = (g16 & 3) >> 1;
+    va0 = (uint32_t)(gbit * kCPS + row * 32 + lhalf * 16 + (g16 & 1) * 8);
+    va1 = (uint32_t)(gbit * kCPS + (row + 8) * 32 + (lhalf ^ 1) * 16 + (g16 & 1) * 8);
   }
 
   // K fragment: keys 32*mt + l32, dims 16*st + 8*half .. +7 (A operand of S^T = K Q^T)
   __device__ __forceinline__ bf16x8 kfrag(const lds_u8* kb, int st, int mt) const {
-    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kb + ka + st * 2048 + mt * 1024);
+    return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(kb + ka + st * kCPS + mt * 1024);
   }
   // V^T fragment for k-step ks4 (keys 16*ks4 .. +15) and dims 32*dt .. +31:
   // two transposing reads; within each group of 16 lanes, lane j points at
   // 4 consecutive dims of one key and lane i receives one dim of 4 keys.
   __device__ __forceinline__ bf16x8 vfrag(const lds_u8* vb, int ks4, int dt) const {
-    const lds_u8* p = vb + va + dt * 4096 + ks4 * 512;
-    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
-    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 256));
+    const int off = dt * 2 * kCPS + ks4 * 512;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb + va0 + off));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb + va1 + off));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
 
