@@ -113,15 +113,17 @@ def test_config3_full_depth_sampled():
     del rng
 
 
-@pytest.mark.parametrize("R", [1, 32, 512])
-def test_config4_points_sampled(R):
-    c = config_attn(4, P=4096, R=R, seed=R)
+@pytest.mark.parametrize("P", [512, 1024, 2048, 4096])
+@pytest.mark.parametrize("R", [1, 8, 16, 32, 64, 128, 256, 512])
+def test_config4_points_sampled(P, R):
+    """Append-prefill sweep (Qwen3-32B heads): R causal rows over a prefix P."""
+    c = config_attn(4, P=P, R=R, seed=P + R)
     out, lse = run_attn(c)
-    rows = _sample_rows(c, 32, seed=R)
+    rows = _sample_rows(c, 12, seed=R)
     ref, rlse = oracle.attn_rows(*oracle_inputs(c), c.cache_len, rows, k=c.k, num_blocks=0,
                                  block_len=1, sm_scale=c.sm_scale)
     got = np.stack([out[b, r, h] for b, r, h in rows])
-    assert _report(f"cfg4 P=4096 R={R}", got, ref, TOL["bf16"]) <= TOL["bf16"]
+    assert _report(f"cfg4 P={P} R={R}", got, ref, TOL["bf16"]) <= TOL["bf16"]
 
 
 def test_deterministic_and_split_independent():
