@@ -53,3 +53,55 @@ def run_attn(case, layer=0, num_splits=0, cache_len=None, max_cache_len=None, wi
 def oracle_inputs(case, layer=0):
     return (case.q[layer], case.k_step[layer], case.v_step[layer], case.k_cache[layer],
             case.v_cache[layer])
+
+
+NEAR = 1e-5  # near-tie band of the sampler comparison (fraction of the total mass / of the accept probability)
+
+
+def draw_candidates(ar_logits, diff_logits, b, n, u_last, temperature=1.0, eps=NEAR):
+    """Tokens whose inverse-CDF interval meets [target - eps*total, target + eps*total].
+
+    For a draw the oracle flags as a near-tie, the GPU's token must be one of
+    these: a different rounding of the running sum can only move the draw
+    across a boundary that lies inside the band.
+    """
+    import oracle
+
+    k = ar_logits.shape[1] - 1
+    p = oracle.softmax_t(ar_logits[b, n], temperature)
+    if n < k:
+        w = np.maximum(0.0, p - oracle.softmax_t(diff_logits[b, n], temperature))
+        if w.sum() == 0.0:
+            w = p
+    else:
+        w = p
+    cs = np.cumsum(w)
+    total = cs[-1]
+    target = float(u_last) * total
+    lo = cs - w
+    return np.nonzero((cs > target - eps * total) & (lo < target + eps * total) & (w > 0))[0]
+
+
+def check_samples(ref, acc, nxt, ar_logits, diff_logits, uniforms, temperature=1.0):
+    """Compare GPU (accept_len, next_token) with the oracle's SampleResult.
+
+    Accept lengths must match unless an acceptance test the oracle consulted
+    is a near-tie. With equal accept lengths the token must match, or (for a
+    draw the oracle flags as a near-tie) lie in the band of boundary tokens.
+    Returns (number of accept near-ties excused, number of draw near-ties).
+    """
+    B = len(acc)
+    k = ar_logits.shape[1] - 1
+    excused = draw_near = 0
+    for b in range(B):
+        if ref.accept_margin[b] < NEAR:
+            excused += 1
+            continue
+        assert acc[b] == ref.accept_len[b], (b, int(acc[b]), int(ref.accept_len[b]))
+        if ref.draw_margin[b] < NEAR:
+            draw_near += 1
+            cand = draw_candidates(ar_logits, diff_logits, b, int(acc[b]), uniforms[b, k], temperature)
+            assert nxt[b] in cand, (b, int(nxt[b]), cand[:8])
+        else:
+            assert nxt[b] == ref.next_token[b], (b, int(nxt[b]), int(ref.next_token[b]))
+    return excused, draw_near

@@ -17,6 +17,7 @@ import torch
 
 import oracle
 from tidar_synth import bf16_bits_to_f32, bf16_round, config_attn, sampler_case
+from tests.gpu_util import check_samples
 
 pytestmark = pytest.mark.gpu
 
@@ -87,9 +88,8 @@ def test_config5_ragged_multistep():
         acc = step.accept_len.cpu().numpy()
         nxt = step.next_token.cpu().numpy()
         ref = oracle.reject_sample(sc.ar_logits, sc.diff_logits, sc.drafts, sc.uniforms)
-        near = (ref.accept_margin < 1e-5) | (ref.draw_margin < 1e-5)
-        near_ties += int(near.sum())
-        assert (((acc == ref.accept_len) & (nxt == ref.next_token)) | near).all()
+        excused, draw_near = check_samples(ref, acc, nxt, sc.ar_logits, sc.diff_logits, sc.uniforms)
+        near_ties += excused + draw_near
         committed.extend((acc + 1).tolist())
 
         # commit: the oracle appends the accepted drafts the GPU chose

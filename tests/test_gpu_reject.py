@@ -1,9 +1,10 @@
 """GPU parity of tidar_reject_sample against the fp64 oracle.
 
-Accept lengths and tokens must match bit for bit given the same uniforms,
-except draws the oracle marks as near-ties (|u - min(1, rho)| < 1e-5 for a
-consulted acceptance test, or the draw within 1e-5 of the total mass of a
-CDF boundary); those are counted and printed, not failed.
+Accept lengths and tokens must match bit for bit given the same uniforms.
+Exceptions, counted and printed: a sequence whose consulted acceptance test
+is a near-tie (|u - min(1, rho)| < 1e-5) is excused; a draw within 1e-5 of
+the total mass of a CDF boundary must return one of the tokens whose interval
+meets that band.
 """
 import json
 import os
@@ -17,6 +18,7 @@ from scipy.special import softmax as sp_softmax
 import ar_self_speculative_amd as tidar
 import oracle
 from tidar_synth import config_sampler, sampler_case
+from tests.gpu_util import check_samples
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -49,12 +51,11 @@ def compare(case, name):
                                case.temperature)
     acc, nxt, ratio = gpu_reject(case.ar_logits, case.diff_logits, case.drafts, case.uniforms,
                                  case.temperature)
-    near = (ref.accept_margin < NEAR) | (ref.draw_margin < NEAR)
     mism = (acc != ref.accept_len) | (nxt != ref.next_token)
-    bad = mism & ~near
-    print(f"[parity] {name}: B={case.batch} mismatches={int(mism.sum())} near-ties={int(near.sum())} "
-          f"mean accept={ref.accept_len.mean():.2f}", flush=True)
-    assert not bad.any(), np.nonzero(bad)
+    excused, draw_near = check_samples(ref, acc, nxt, case.ar_logits, case.diff_logits, case.uniforms,
+                                       case.temperature)
+    print(f"[parity] {name}: B={case.batch} mismatches={int(mism.sum())} accept near-ties={excused} "
+          f"draw near-ties={draw_near} mean accept={ref.accept_len.mean():.2f}", flush=True)
     finite = np.isfinite(ref.ratio)
     np.testing.assert_allclose(ratio[finite], ref.ratio[finite], rtol=2e-5)
     return ref
