@@ -36,6 +36,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16;
 
 constexpr int kBM = 128;          // packed query rows per workgroup (bf16 path)
@@ -322,9 +323,10 @@ struct Wave {
   //            tile's probabilities (from s_cur);
   //   phase B: this tile's O^T += V^T P^T MFMAs interleaved with the row
   //            maxima of the next tile (NEXT).
-  // Operand fragments are read LA MFMA slots ahead; sched_barrier(0) pins
-  // each slot so the LDS, matrix and vector pipes overlap.
-  static constexpr int LA = 1;
+  // Operand fragments are read LA (K, phase A) and LB (V, phase B) MFMA
+  // slots ahead; sched_barrier(0) pins each slot so the LDS, matrix and
+  // vector pipes overlap.
+  static constexpr int LA = 2, LB = 2;
   // There is no branch between the phases: code motion across one would undo
   // the interleaving.
   template <bool QK, bool NEXT>
@@ -363,10 +365,10 @@ struct Wave {
     constexpr int NB = 4 * DT;
     bf16x8 vf[NB];
 #pragma unroll
-    for (int j = 0; j < LA; ++j) vf[j] = vfrag(vb_cur, j / DT, j % DT);
+    for (int j = 0; j < LB; ++j) vf[j] = vfrag(vb_cur, j / DT, j % DT);
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      if (j + LA < NB) vf[j + LA] = vfrag(vb_cur, (j + LA) / DT, (j + LA) % DT);
+      if (j + LB < NB) vf[j + LB] = vfrag(vb_cur, (j + LB) / DT, (j + LB) % DT);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int nt = 0; nt < NQT; ++nt)
@@ -617,21 +619,25 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
   // computes QK^T(t+1), P(t) and PV(t).
   typename W::S sA, sB;
   if (ntot > 0) {
+    // Only Q and K[0] are waited for before the first QK^T; V[0] and K[1]
+    // arrive while it and the first maxima run (every workgroup starts at
+    // once, so this start-up burst is what the first wait pays for).
     const TileSrc t0 = seq.at(0);
     copy_tile<D, WAVES>(make_rsrc(t0.k, t0.bytes), t0.vo, t0.row0, t0.row_bytes, KB[0], wave);
+    wait_copies();
+    __syncthreads();
     copy_tile<D, WAVES>(make_rsrc(t0.v, t0.bytes), t0.vo, t0.row0, t0.row_bytes, VB[0], wave);
     if (ntot > 1) {
       const TileSrc t1 = seq.at(1);
       copy_tile<D, WAVES>(make_rsrc(t1.k, t1.bytes), t1.vo, t1.row0, t1.row_bytes, KB[1], wave);
     }
-    wait_copies();
-    __syncthreads();
     st.qk(KB[0], sA);
     if (t0.local)
       W::template mask<true>(sA, lane, t0.nvalid, t0.c_base, rules);
     else if (t0.nvalid < kBN)
       W::template mask<false>(sA, lane, t0.nvalid, 0, rules);
     st.tile_max(sA, sl2);
+    wait_copies();
   }
   // iterations whose next tile is a full prefix tile run a loop of their own
   const int tmain = __builtin_amdgcn_readfirstlane(max(0, min(nk / kBN, ntot) - 1));
@@ -651,38 +657,65 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
                              par ? VB[0] : VB[1], seq, t, wave, lane, rules, sl2, sA, sB);
   }
 
-  // o[nt][dt][v] holds O^T[d = 32*dt + 8*(v/4) + 4*half + v%4][this lane's row]
+  // o[nt][dt][v] holds O^T[d = 32*dt + 8*(v/4) + 4*half + v%4][this lane's row].
+  // Each 32-row group is normalised, rounded to bf16 and staged row-major in
+  // LDS (row pitch 2*D + 16 bytes; the row's output index sits in the
+  // padding), then written back as whole rows with 16-byte stores: a store
+  // instruction covers complete 128-byte lines instead of 8-byte pieces of
+  // 32 different rows. WAVES * NQT == 4, so the four groups take one tile
+  // buffer each.
+  constexpr int PITCH = 2 * D + 16;
+  constexpr int CHUNKS = D / 8;                 // 16-byte pieces per row
+  constexpr int PASSES = 32 * CHUNKS / 64;      // store instructions per group
+  static_assert(WAVES * NQT == 4 && 32 * PITCH <= L::TILE_BYTES, "staging does not fit");
+  __syncthreads();  // every wave is done with the last tile's K and V
 #pragma unroll
   for (int nt = 0; nt < NQT; ++nt) {
+    const int grp = wave * NQT + nt;
+    lds_u8* const stage = grp == 0 ? KB[0] : grp == 1 ? KB[1] : grp == 2 ? VB[0] : VB[1];
     const float ltot = half_sum(st.l[nt]);
     const int m = qt * BM + wave * WROWS + 32 * nt + l32;
-    if (m >= M) continue;
-    const int r = m / p.g;
-    const int h = kvh * p.g + (m - r * p.g);
-    const size_t orow = ((size_t)(b * p.R + r) * p.Hq + h);
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    u16* op;
-    if (p.S == 1) {
-      op = reinterpret_cast<u16*>(p.out) + orow * D;
-      if (p.lse && half == 0) p.lse[orow] = (st.m[nt] + log2f(ltot)) * 0.69314718055994531f;
-    } else {
-      // normalised partial in bf16 plus its log2-domain log-sum-exp
-      const size_t prow = (size_t)s * p.B * p.R * p.Hq + orow;
-      op = reinterpret_cast<u16*>(p.part_o) + prow * D;
-      if (half == 0) p.part_lse[prow] = ltot > 0.f ? st.m[nt] + log2f(ltot) : kNegInf;
+    if (half == 0) {
+      const int r = m / p.g;
+      const uint32_t orow = (uint32_t)((b * p.R + r) * p.Hq + kvh * p.g + (m - r * p.g));
+      *reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(stage + l32 * PITCH + 2 * D) =
+          m < M ? orow : 0xFFFFFFFFu;
+    }
+    if (m < M && half == 0) {
+      const int r = m / p.g;
+      const size_t orow = ((size_t)(b * p.R + r) * p.Hq + kvh * p.g + (m - r * p.g));
+      if (p.S == 1) {
+        if (p.lse) p.lse[orow] = (st.m[nt] + log2f(ltot)) * 0.69314718055994531f;
+      } else {
+        // log2-domain log-sum-exp of this split's partial
+        p.part_lse[(size_t)s * p.B * p.R * p.Hq + orow] = ltot > 0.f ? st.m[nt] + log2f(ltot) : kNegInf;
+      }
     }
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int d = 32 * dt + 8 * i + 4 * half;
-        ushort4 pk;
-        pk.x = f32_to_bf16_bits(st.o[nt][dt][4 * i + 0] * inv);
-        pk.y = f32_to_bf16_bits(st.o[nt][dt][4 * i + 1] * inv);
-        pk.z = f32_to_bf16_bits(st.o[nt][dt][4 * i + 2] * inv);
-        pk.w = f32_to_bf16_bits(st.o[nt][dt][4 * i + 3] * inv);
-        *reinterpret_cast<ushort4*>(op + d) = pk;
+        bf16x4 v;
+        v[0] = (__bf16)(st.o[nt][dt][4 * i + 0] * inv);
+        v[1] = (__bf16)(st.o[nt][dt][4 * i + 1] * inv);
+        v[2] = (__bf16)(st.o[nt][dt][4 * i + 2] * inv);
+        v[3] = (__bf16)(st.o[nt][dt][4 * i + 3] * inv);
+        *reinterpret_cast<__attribute__((address_space(3))) bf16x4*>(stage + l32 * PITCH + 2 * d) = v;
       }
+    __syncthreads();  // the group's rows are complete in LDS (cheap: once per workgroup)
+    u16* const obase = p.S == 1 ? reinterpret_cast<u16*>(p.out)
+                                : reinterpret_cast<u16*>(p.part_o) + (size_t)s * p.B * p.R * p.Hq * D;
+#pragma unroll
+    for (int j = 0; j < PASSES; ++j) {
+      const int f = j * 64 + lane;
+      const int row = f / CHUNKS, c = f % CHUNKS;
+      const uint32_t orow = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(stage + row * PITCH + 2 * D);
+      if (orow == 0xFFFFFFFFu) continue;  // past the last query row
+      *reinterpret_cast<u32x4*>(obase + (size_t)orow * D + 8 * c) =
+          *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(stage + row * PITCH + 16 * c);
+    }
   }
 }
 
