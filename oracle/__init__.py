@@ -14,7 +14,8 @@ Contents (every function cites the passage it follows):
   matrix built from the region rules, then masked softmax. Used to pin
   ``attn_step``.
 * ``reject.reject_sample``  - AR rejection sampling of the diffusion drafts
-  with residual / bonus resampling by inverse CDF.
+  with residual / bonus resampling by inverse CDF; ``trust_ar`` mixes the
+  AR and diffusion logits of the targets (``reject.target_logits``).
 * ``commit.kv_commit``      - exact-KV append of accepted drafts.
 
 All floating point is fp64. Pins live in ``tests/test_oracle_*.py``; no part
@@ -22,11 +23,11 @@ is "parity unpinned".
 """
 from .attention import attn_step, attn_rows, local_keys, visible_local_count
 from .dense import attn_dense, hybrid_mask_matrix
-from .reject import reject_sample, invcdf, softmax_t, SampleResult, selected_block_rows
+from .reject import reject_sample, invcdf, softmax_t, SampleResult, selected_block_rows, target_logits
 from .commit import kv_commit
 
 __all__ = [
     "attn_step", "attn_rows", "local_keys", "visible_local_count", "attn_dense",
     "hybrid_mask_matrix", "reject_sample", "invcdf", "softmax_t",
-    "SampleResult", "selected_block_rows", "kv_commit",
+    "SampleResult", "selected_block_rows", "target_logits", "kv_commit",
 ]

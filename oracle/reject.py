@@ -16,6 +16,12 @@ Sources:
   token is drawn from the last AR distribution p_k. The committed tokens are
   then distributed exactly as the AR chain.
 
+* TiDAR review, "设计取舍" (trust AR vs trust diffusion, Fig. 6): at
+  verification the AR and diffusion logits can be mixed with a weight lambda;
+  the quality barely moves across lambda, which the review reads as the AR
+  rejection-sampling step (not either mode's knowledge) setting the
+  quality/speed trade-off.
+
 Readings where the pages are silent:
 * p_i = softmax(ar_logits[i] / T) for i = 0..k, q_i = softmax(diff_logits[i]/T)
   for i = 0..k-1; row i of the AR logits is the target for draft d_{i+1} and
@@ -26,6 +32,14 @@ Readings where the pages are silent:
 * An all-zero residual (possible only through rounding) falls back to p_n.
 * invcdf(w, u): smallest token id t (scanning in id order) whose running sum
   of w exceeds u * sum(w); if rounding leaves none, the largest t with w_t > 0.
+* Trust mixing (trust_ar = lambda): the target of draft d_{i+1} becomes
+  softmax((lambda * ar_logits[i] + (1 - lambda) * diff_logits[i]) / T), mixed
+  in logit space on the diffusion row that proposed the draft; the proposal
+  q_i is unchanged, and the bonus row k has no diffusion counterpart so it
+  stays pure AR. lambda = 1 is the plain sampler (trust AR) and lambda = 0
+  takes the diffusion logits as the target (trust diffusion); these two end
+  points use the respective logits as they are, so infinite logits need no
+  0 * inf.
 """
 from __future__ import annotations
 
@@ -74,12 +88,31 @@ class SampleResult:
     residual_mass: np.ndarray  # float64 [B]: sum(max(0, p_n - q_n)), or 1 for the bonus draw
 
 
-def reject_sample(ar_logits, diff_logits, drafts, uniforms, temperature: float = 1.0) -> SampleResult:
+def target_logits(ar_row, diff_row, trust_ar: float = 1.0) -> np.ndarray:
+    """Logits of the verification target for one draft position (fp64).
+
+    diff_row is None for the bonus row. Mixing as in the review's trust
+    AR / trust diffusion comparison: lambda * AR + (1 - lambda) * diffusion.
+    """
+    a = np.asarray(ar_row, np.float64)
+    if diff_row is None or trust_ar == 1.0:
+        return a
+    d = np.asarray(diff_row, np.float64)
+    if trust_ar == 0.0:
+        return d
+    return trust_ar * a + (1.0 - trust_ar) * d
+
+
+def reject_sample(ar_logits, diff_logits, drafts, uniforms, temperature: float = 1.0,
+                  trust_ar: float = 1.0) -> SampleResult:
     """Verify k drafts per sequence and draw the correction / bonus token.
 
     ar_logits [B, k+1, V], diff_logits [B, k, V], drafts [B, k] int,
-    uniforms [B, k+1]. Returns accept lengths n in 0..k and next_token c.
+    uniforms [B, k+1]; trust_ar in [0, 1] mixes the targets (1 = plain AR).
+    Returns accept lengths n in 0..k and next_token c.
     """
+    if not (0.0 <= trust_ar <= 1.0):
+        raise ValueError("trust_ar must lie in [0, 1]")
     ar_logits = np.asarray(ar_logits)
     diff_logits = np.asarray(diff_logits)
     B, kp1, V = ar_logits.shape
@@ -91,7 +124,8 @@ def reject_sample(ar_logits, diff_logits, drafts, uniforms, temperature: float =
     dmarg = np.zeros(B)
     rmass = np.zeros(B)
     for b in range(B):
-        p = [softmax_t(ar_logits[b, i], temperature) for i in range(k + 1)]
+        p = [softmax_t(target_logits(ar_logits[b, i], diff_logits[b, i] if i < k else None, trust_ar),
+                       temperature) for i in range(k + 1)]
         q = [softmax_t(diff_logits[b, i], temperature) for i in range(k)]
         for i in range(k):
             d = int(drafts[b, i])

@@ -5,6 +5,10 @@ special cases that reduce to plain categorical sampling, the closed-form
 acceptance law of speculative sampling (P(n >= i) = prod_{m<i} alpha_m with
 alpha_m = sum_t min(p_m(t), q_m(t))), and the empirical law of the committed
 tokens, which must equal the AR distributions p_0 and p_1 (chi-square).
+With trust mixing (TiDAR review, 设计取舍, Fig. 6) the same laws hold for the
+mixed targets softmax(lambda * AR + (1 - lambda) * diffusion): lambda = 0
+accepts every draft, and the first committed token follows the logit-space
+mixture, not the probability-space one.
 """
 import json
 import os
@@ -38,7 +42,8 @@ def _scan_invcdf(w, u):
 def test_golden_hand_examples(case):
     ar = np.log(np.array(case["p"]))[None]
     diff = np.log(np.array(case["q"]))[None]
-    res = oracle.reject_sample(ar, diff, np.array([case["drafts"]]), np.array([case["uniforms"]]))
+    res = oracle.reject_sample(ar, diff, np.array([case["drafts"]]), np.array([case["uniforms"]]),
+                               trust_ar=case.get("trust_ar", 1.0))
     assert res.accept_len[0] == case["expect_n"]
     assert res.next_token[0] == case["expect_c"]
     np.testing.assert_allclose(res.ratio[0], case["ratio"], rtol=1e-12)
@@ -127,6 +132,52 @@ def test_committed_tokens_follow_ar_chain():
     assert chi2.pvalue > 1e-3, chi2
     # and the law is far from the proposal, so the test has power
     assert stats.chisquare(obs, N * q[0]).pvalue < 1e-6
+
+
+def test_trust_diffusion_accepts_every_draft():
+    c = sampler_case(batch=64, k=5, vocab=97, ar_sigma=2.0, diff_mode="independent",
+                     diff_sigma=1.0, seed=9)
+    res = oracle.reject_sample(c.ar_logits, c.diff_logits, c.drafts, c.uniforms, trust_ar=0.0)
+    assert (res.accept_len == 5).all()
+    np.testing.assert_allclose(res.ratio, 1.0, rtol=1e-12)
+    for b in range(64):
+        p = sp_softmax(c.ar_logits[b, 5].astype(np.float64))   # bonus row stays pure AR
+        assert res.next_token[b] == _scan_invcdf(p, float(c.uniforms[b, 5]))
+
+
+def test_trust_one_is_the_plain_sampler():
+    c = sampler_case(batch=32, k=4, vocab=80, ar_sigma=2.0, diff_mode="noisy", diff_sigma=0.7, seed=10)
+    a = oracle.reject_sample(c.ar_logits, c.diff_logits, c.drafts, c.uniforms)
+    b = oracle.reject_sample(c.ar_logits, c.diff_logits, c.drafts, c.uniforms, trust_ar=1.0)
+    assert (a.accept_len == b.accept_len).all() and (a.next_token == b.next_token).all()
+    with pytest.raises(ValueError):
+        oracle.reject_sample(c.ar_logits, c.diff_logits, c.drafts, c.uniforms, trust_ar=1.5)
+
+
+def test_trust_mixture_laws():
+    """lambda = 0.4: acceptance law and first-token law of the logit-space mixture."""
+    V, k, N, lam = 12, 2, 100_000, 0.4
+    rng = np.random.default_rng(11)
+    ar = rng.normal(0, 2.0, size=(k + 1, V))
+    diff = rng.normal(0, 2.0, size=(k, V))
+    q = sp_softmax(diff, axis=-1)
+    target = sp_softmax(lam * ar[:k] + (1 - lam) * diff, axis=-1)
+    drafts = np.stack([rng.choice(V, size=N, p=q[i]) for i in range(k)], axis=1)
+    u = rng.random((N, k + 1))
+    res = oracle.reject_sample(np.broadcast_to(ar, (N, k + 1, V)), np.broadcast_to(diff, (N, k, V)),
+                               drafts, u, trust_ar=lam)
+    alpha = np.minimum(target, q).sum(axis=1)
+    for i in range(1, k + 1):
+        expect = np.prod(alpha[:i])
+        got = (res.accept_len >= i).mean()
+        assert abs(got - expect) < 5 * np.sqrt(expect * (1 - expect) / N) + 1e-9, (i, got, expect)
+    first = np.where(res.accept_len >= 1, drafts[:, 0], res.next_token)
+    obs = np.bincount(first, minlength=V)
+    assert stats.chisquare(obs, N * target[0]).pvalue > 1e-3
+    # power: the law differs from the probability-space mixture and from both modes
+    prob_mix = lam * sp_softmax(ar[0]) + (1 - lam) * q[0]
+    for other in (prob_mix, sp_softmax(ar[0]), q[0]):
+        assert stats.chisquare(obs, N * other / other.sum()).pvalue < 1e-6
 
 
 def test_selected_block_rows():
