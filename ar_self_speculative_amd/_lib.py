@@ -34,7 +34,7 @@ DEV_DRAFT_RANGE = 16
 EXPORTS = (
     "tidar_status_string", "tidar_last_error", "tidar_version",
     "tidar_attn_workspace_bytes", "tidar_attn_step", "tidar_kv_commit",
-    "tidar_reject_workspace_bytes", "tidar_reject_sample",
+    "tidar_reject_workspace_bytes", "tidar_reject_sample", "tidar_reject_sample_trust",
 )
 
 
@@ -74,6 +74,9 @@ def load() -> ctypes.CDLL:
     lib.tidar_reject_workspace_bytes.argtypes = [i32, i32, i32]
     lib.tidar_reject_sample.restype = ctypes.c_int
     lib.tidar_reject_sample.argtypes = [i32, i32, i32, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp]
+    lib.tidar_reject_sample_trust.restype = ctypes.c_int
+    lib.tidar_reject_sample_trust.argtypes = [i32, i32, i32, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float,
+                                              vp, vp, vp, vp, vp, sz, vp]
     return lib
 
 
@@ -181,7 +184,7 @@ def reject_workspace_bytes(batch: int, k: int, vocab: int) -> int:
 
 
 def reject_sample(*, ar_logits, diff_logits, drafts, uniforms, accept_len, next_token, ratio=None,
-                  dev_status=None, workspace, temperature: float = 1.0, stream=None):
+                  dev_status=None, workspace, temperature: float = 1.0, trust_ar: float = 1.0, stream=None):
     B, kp1, V = ar_logits.shape
     k = kp1 - 1
     _dev(ar_logits, torch.float32, "ar_logits")
@@ -193,7 +196,11 @@ def reject_sample(*, ar_logits, diff_logits, drafts, uniforms, accept_len, next_
     _dev(ratio, torch.float32, "ratio", allow_none=True)
     _dev(dev_status, torch.int32, "dev_status", allow_none=True)
     _dev(workspace, None, "workspace")
-    _check(_lib.tidar_reject_sample(B, k, V, _ptr(ar_logits), _ptr(diff_logits), _ptr(drafts),
-                                    _ptr(uniforms), float(temperature), _ptr(accept_len),
-                                    _ptr(next_token), _ptr(ratio), _ptr(dev_status), _ptr(workspace),
-                                    workspace.numel() * workspace.element_size(), _stream(stream)))
+    args = (_ptr(accept_len), _ptr(next_token), _ptr(ratio), _ptr(dev_status), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    if trust_ar == 1.0:
+        _check(_lib.tidar_reject_sample(B, k, V, _ptr(ar_logits), _ptr(diff_logits), _ptr(drafts),
+                                        _ptr(uniforms), float(temperature), *args))
+    else:
+        _check(_lib.tidar_reject_sample_trust(B, k, V, _ptr(ar_logits), _ptr(diff_logits), _ptr(drafts),
+                                              _ptr(uniforms), float(temperature), float(trust_ar), *args))

@@ -207,6 +207,15 @@ int tidar_reject_sample(int32_t batch, int32_t k, int32_t vocab, const float* ar
                         const int32_t* drafts, const float* uniforms, float temperature, int32_t* accept_len,
                         int32_t* next_token, float* ratio, int32_t* dev_status, void* workspace,
                         size_t workspace_bytes, void* stream) {
+  return tidar_reject_sample_trust(batch, k, vocab, ar_logits, diff_logits, drafts, uniforms, temperature, 1.0f,
+                                   accept_len, next_token, ratio, dev_status, workspace, workspace_bytes, stream);
+}
+
+int tidar_reject_sample_trust(int32_t batch, int32_t k, int32_t vocab, const float* ar_logits,
+                              const float* diff_logits, const int32_t* drafts, const float* uniforms,
+                              float temperature, float trust_ar, int32_t* accept_len, int32_t* next_token,
+                              float* ratio, int32_t* dev_status, void* workspace, size_t workspace_bytes,
+                              void* stream) {
   if (batch < 1 || k < 0 || vocab < 1) return fail(TIDAR_E_INVALID, "need batch >= 1, k >= 0, vocab >= 1");
   if (k > tidar::reject_max_k()) return fail(TIDAR_E_UNSUPPORTED, "k = %d exceeds %d", k, tidar::reject_max_k());
   tidar::RejectParams p{};
@@ -219,6 +228,7 @@ int tidar_reject_sample(int32_t batch, int32_t k, int32_t vocab, const float* ar
   if ((long)batch * (k + 1) * (long)vocab > 0x7fffffffL || (long)batch * (2 * k + 1) * p.nchunks > 0x7fffffffL)
     return fail(TIDAR_E_UNSUPPORTED, "logits too large");
   if (!(temperature > 0.f) || !isfinite(temperature)) return fail(TIDAR_E_INVALID, "temperature must be > 0");
+  if (!(trust_ar >= 0.f && trust_ar <= 1.f)) return fail(TIDAR_E_INVALID, "trust_ar must lie in [0, 1]");
   if (!ar_logits || !uniforms || !accept_len || !next_token)
     return fail(TIDAR_E_INVALID, "a required pointer is NULL");
   if (k > 0 && (!diff_logits || !drafts)) return fail(TIDAR_E_INVALID, "diff_logits and drafts required when k > 0");
@@ -233,6 +243,9 @@ int tidar_reject_sample(int32_t batch, int32_t k, int32_t vocab, const float* ar
   p.drafts = drafts;
   p.uniforms = uniforms;
   p.inv_temp = 1.f / temperature;
+  p.mix = trust_ar == 1.f ? 0 : trust_ar == 0.f ? 2 : 1;
+  p.lam = trust_ar;
+  p.mu = 1.f - trust_ar;
   p.accept_len = accept_len;
   p.next_token = next_token;
   p.ratio = ratio;

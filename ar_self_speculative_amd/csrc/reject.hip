@@ -17,6 +17,12 @@
 //   3. rej_pick  : per sequence, locates the chunk whose running mass passes
 //                  u * total, then the token inside it (inverse CDF in token
 //                  id order).
+// Trust mixing (TiDAR review, 设计取舍: trust AR vs trust diffusion logits,
+// Fig. 6) replaces the target logits of rows 0..k-1 by lam * AR +
+// (1 - lam) * diffusion of the same position; the statistics, the gathered
+// draft probabilities and the draw weights all evaluate the mixed logit the
+// same way, fmaf(lam, a, mu * d). lam = 1 and lam = 0 read the AR or the
+// diffusion row as it is.
 #include "tidar_internal.h"
 
 #include <math.h>
@@ -108,10 +114,21 @@ __global__ __launch_bounds__(kThreads) void rej_stats_kernel(RejectParams p) {
   const int row = blockIdx.x / p.nchunks;
   const int nrows = 2 * p.k + 1;
   const int b = row / nrows, rr = row % nrows;
-  const float* x = row_ptr(p, b, rr);
+  const bool target = rr < p.k;  // a verification target (not the bonus row)
+  const float* x = row_ptr(p, b, target && p.mix == 2 ? p.k + 1 + rr : rr);
   const int e0 = c * kChunk, e1 = min(e0 + kChunk, p.V);
+  const bool vec4 = (p.V & 3) == 0;
   float v[kPer];
-  load_chunk(x, e0, e1, p.inv_temp, (p.V & 3) == 0, v);
+  if (target && p.mix == 1) {
+    // mixed target: (lam * a + mu * d) / T, formed exactly as in the draws
+    float w[kPer];
+    load_chunk(x, e0, e1, 1.f, vec4, v);
+    load_chunk(row_ptr(p, b, p.k + 1 + rr), e0, e1, 1.f, vec4, w);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) v[j] = fmaf(p.lam, v[j], p.mu * w[j]) * p.inv_temp;
+  } else {
+    load_chunk(x, e0, e1, p.inv_temp, vec4, v);
+  }
   float mx = kNegInf;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) mx = fmaxf(mx, v[j]);
@@ -125,28 +142,46 @@ __global__ __launch_bounds__(kThreads) void rej_stats_kernel(RejectParams p) {
   if (threadIdx.x == 0) p.row_stats[((size_t)b * nrows + rr) * p.nchunks + c] = make_float2(mx, s);
 }
 
+// The mixed logit of a verification target (mix == 1), as rej_stats forms it.
+__device__ __forceinline__ float mix_logit(const RejectParams& p, float a, float d) {
+  return fmaf(p.lam, a, p.mu * d);
+}
+
 // Weight of token t for the final draw: residual max(0, p_n - q_n) after a
 // rejection, p_k for the bonus draw, p_n for the all-zero-residual fallback.
-// Probabilities are evaluated as 2^(x * s - m * log2 e) / z from the merged
-// row statistics (m, z) of the temperature-scaled logits.
+// Probabilities are evaluated as 2^(y * s - m * log2 e) / z from the merged
+// row statistics (m, z) of the temperature-scaled logits, y being the
+// target's logit (AR, mixed, or diffusion; the bonus row is always AR).
 struct DrawRows {
-  const float* a;  // AR row
-  const float* q;  // diffusion row, or nullptr for a plain AR draw
+  const float* a;  // AR row (unused when the target is the diffusion row)
+  const float* q;  // diffusion row of the same position, or nullptr for the bonus draw
+  bool sub;        // subtract q: the residual after a rejection
+  int mix;         // target logits: 0 = a, 1 = lam * a + mu * q, 2 = q
+  float lam, mu;
   float s;         // log2(e) / T
-  float ba, ra;    // m_a * log2(e), 1 / z_a
+  float ba, ra;    // m_target * log2(e), 1 / z_target
   float bq, rq;
-  __device__ __forceinline__ void init(const RejectParams& p, const float* arow, float2 sa, const float* qrow,
-                                       float2 sq) {
+  __device__ __forceinline__ void init(const RejectParams& p, int b, int n, const float2* mz) {
     const float l2e = 1.4426950408889634f;
-    a = arow;
-    q = qrow;
+    const int k = p.k;
+    a = row_ptr(p, b, n);
+    q = n < k ? row_ptr(p, b, k + 1 + n) : nullptr;
+    sub = n < k;
+    mix = n < k ? p.mix : 0;
+    lam = p.lam;
+    mu = p.mu;
     s = p.inv_temp * l2e;
+    const float2 sa = mz[n], sq = n < k ? mz[k + 1 + n] : make_float2(0.f, 1.f);
     ba = sa.x * l2e;
     ra = 1.f / sa.y;
-    bq = qrow ? sq.x * l2e : 0.f;
-    rq = qrow ? 1.f / sq.y : 0.f;
+    bq = q ? sq.x * l2e : 0.f;
+    rq = q ? 1.f / sq.y : 0.f;
   }
-  __device__ __forceinline__ float pa(float x) const { return __builtin_amdgcn_exp2f(fmaf(x, s, -ba)) * ra; }
+  __device__ __forceinline__ bool needs_a() const { return mix != 2; }
+  __device__ __forceinline__ float target(float xa, float xq) const {
+    return mix == 0 ? xa : mix == 2 ? xq : fmaf(lam, xa, mu * xq);
+  }
+  __device__ __forceinline__ float pt(float y) const { return __builtin_amdgcn_exp2f(fmaf(y, s, -ba)) * ra; }
   __device__ __forceinline__ float pq(float x) const { return __builtin_amdgcn_exp2f(fmaf(x, s, -bq)) * rq; }
 };
 
@@ -208,13 +243,14 @@ __global__ __launch_bounds__(kThreads) void rej_resid_kernel(RejectParams p) {
   // the statistics merge
   const int i = threadIdx.x;
   int d = -1;
-  float da = 0.f, dq = 0.f;  // logits of draft i under the AR and diffusion rows
+  float da = 0.f, dq = 0.f;  // logits of draft i under its target and diffusion rows
   if (i < k) {
     d = p.drafts[(size_t)b * k + i];
     uni[i] = p.uniforms[(size_t)b * (k + 1) + i];
     if (d >= 0 && d < p.V) {
-      da = row_ptr(p, b, i)[d];
       dq = row_ptr(p, b, k + 1 + i)[d];
+      da = p.mix == 2 ? dq : row_ptr(p, b, i)[d];
+      if (p.mix == 1) da = mix_logit(p, da, dq);  // the target's logit at the draft
     }
   }
   // per-row statistics: stage every (row, chunk) pair of this sequence in
@@ -275,8 +311,7 @@ __global__ __launch_bounds__(kThreads) void rej_resid_kernel(RejectParams p) {
     }
   }
   DrawRows dr;
-  dr.init(p, row_ptr(p, b, n), mz[n], n < k ? row_ptr(p, b, k + 1 + n) : nullptr,
-          n < k ? mz[k + 1 + n] : make_float2(0.f, 1.f));
+  dr.init(p, b, n, mz);
   // per chunk: mass of the draw distribution, and of p_n alone (the
   // fallback when the residual vanishes through rounding)
   const int e0 = c * kChunk, e1 = min(e0 + kChunk, p.V);
@@ -284,17 +319,17 @@ __global__ __launch_bounds__(kThreads) void rej_resid_kernel(RejectParams p) {
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int t = min(e0 + threadIdx.x + kThreads * j, e1 - 1);
-    xa[j] = dr.a[t];
+    xa[j] = dr.needs_a() ? dr.a[t] : 0.f;
     xq[j] = dr.q ? dr.q[t] : 0.f;
   }
   double acc = 0.0, acc_a = 0.0;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     if (e0 + (int)threadIdx.x + kThreads * j < e1) {
-      const float pa = dr.pa(xa[j]);
-      const float w = dr.q ? fmaxf(0.f, pa - dr.pq(xq[j])) : pa;
+      const float pt = dr.pt(dr.target(xa[j], xq[j]));
+      const float w = dr.sub ? fmaxf(0.f, pt - dr.pq(xq[j])) : pt;
       acc += (double)w;
-      acc_a += (double)pa;
+      acc_a += (double)pt;
     }
   }
   acc = block_sumd(acc, redd);
@@ -313,8 +348,7 @@ __global__ __launch_bounds__(kThreads) void rej_pick_kernel(RejectParams p) {
   const int b = blockIdx.x, k = p.k, nrows = 2 * k + 1;
   const int n = p.decision[2 * b];
   DrawRows dr;
-  dr.init(p, row_ptr(p, b, n), p.row_mz[(size_t)b * nrows + n], n < k ? row_ptr(p, b, k + 1 + n) : nullptr,
-          n < k ? p.row_mz[(size_t)b * nrows + k + 1 + n] : make_float2(0.f, 1.f));
+  dr.init(p, b, n, p.row_mz + (size_t)b * nrows);
   // thread t owns chunks [cpt*t, cpt*t + cpt)
   const int cpt = (p.nchunks + kThreads - 1) / kThreads;
   const int c0 = cpt * threadIdx.x, c1 = min(c0 + cpt, p.nchunks);
@@ -324,7 +358,7 @@ __global__ __launch_bounds__(kThreads) void rej_pick_kernel(RejectParams p) {
   double incl = block_scan_incl(mine, red, &total);
   if (!(total > 0.0)) {
     // the residual vanished through rounding: draw from p_n instead
-    dr.q = nullptr;
+    dr.sub = false;
     mine = 0.0;
     for (int c = c0; c < c1; ++c) mine += (sums[c] = p.resid_sums[((size_t)p.B + b) * p.nchunks + c]);
     incl = block_scan_incl(mine, red, &total);
@@ -363,14 +397,14 @@ __global__ __launch_bounds__(kThreads) void rej_pick_kernel(RejectParams p) {
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int t = min(e0 + (int)threadIdx.x * kPer + j, e1 - 1);
-    w[j] = dr.a[t];
+    w[j] = dr.needs_a() ? dr.a[t] : 0.f;
     xq[j] = dr.q ? dr.q[t] : 0.f;
   }
   double tsum = 0.0;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const float pa = dr.pa(w[j]);
-    w[j] = e0 + (int)threadIdx.x * kPer + j < e1 ? (dr.q ? fmaxf(0.f, pa - dr.pq(xq[j])) : pa) : 0.f;
+    const float pt = dr.pt(dr.target(w[j], xq[j]));
+    w[j] = e0 + (int)threadIdx.x * kPer + j < e1 ? (dr.sub ? fmaxf(0.f, pt - dr.pq(xq[j])) : pt) : 0.f;
     tsum += (double)w[j];
   }
   double ctot;

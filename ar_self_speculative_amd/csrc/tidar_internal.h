@@ -67,6 +67,10 @@ struct RejectParams {
   const int32_t* drafts;
   const float* uniforms;
   float inv_temp;
+  // how the verification targets of rows 0..k-1 are formed: 0 = AR logits,
+  // 1 = lam * AR + mu * diffusion (trust mixing, mu = 1 - lam), 2 = diffusion
+  int mix;
+  float lam, mu;
   int32_t* accept_len;
   int32_t* next_token;
   float* ratio;

@@ -21,9 +21,11 @@ class DecodeStep:
                  head_dim: int, k: int, cache_capacity: int, max_cache_len: int, vocab: int,
                  dtype: int = _lib.DTYPE_BF16, sm_scale: float | None = None,
                  num_blocks: int | None = None, block_len: int | None = None,
-                 num_splits: int = 0, device: str = "cuda", with_lse: bool = False):
+                 num_splits: int = 0, device: str = "cuda", with_lse: bool = False,
+                 trust_ar: float = 1.0):
         self.L, self.B, self.Hq, self.Hkv, self.D = layers, batch, num_q_heads, num_kv_heads, head_dim
         self.k = k
+        self.trust_ar = trust_ar  # weight of the AR logits in the verification targets (1 = plain AR)
         self.num_blocks = k + 1 if num_blocks is None else num_blocks
         self.block_len = k if block_len is None else block_len
         self.R = k + self.num_blocks * self.block_len
@@ -66,8 +68,9 @@ class DecodeStep:
 
     def verify(self, stream=None):
         _lib.reject_sample(ar_logits=self.ar_logits, diff_logits=self.diff_logits, drafts=self.drafts,
-                           uniforms=self.uniforms, accept_len=self.accept_len, next_token=self.next_token, ratio=self.ratio, dev_status=self.dev_status,
-                           workspace=self.rej_ws, stream=stream)
+                           uniforms=self.uniforms, accept_len=self.accept_len, next_token=self.next_token,
+                           ratio=self.ratio, dev_status=self.dev_status, workspace=self.rej_ws,
+                           trust_ar=self.trust_ar, stream=stream)
 
     def commit(self, stream=None):
         _lib.kv_commit(num_layers=self.L, batch=self.B, num_kv_heads=self.Hkv, head_dim=self.D,

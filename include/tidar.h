@@ -181,6 +181,29 @@ int tidar_reject_sample(int32_t batch, int32_t k, int32_t vocab, const float* ar
                         int32_t* dev_status, void* workspace, size_t workspace_bytes,
                         void* stream);
 
+/* ------------------------------------------------------------------------
+ * The same sampler with trust mixing of the verification targets (TiDAR
+ * review, awesome-system-papers wiki, section 设计取舍: trust AR vs trust
+ * diffusion logits, Fig. 6 — the AR and diffusion logits are mixed with a
+ * weight lambda at verification time):
+ *   p_i = softmax((trust_ar * ar_logits[b,i,:] + (1 - trust_ar) * diff_logits[b,i,:]) / T),
+ *         i = 0..k-1, mixed on the diffusion row that proposed d_{i+1};
+ *   p_k = softmax(ar_logits[b,k,:] / T)  (the bonus row has no diffusion row);
+ *   q_i, the acceptance rule, the residual and the draws are unchanged.
+ * trust_ar in [0, 1] (else TIDAR_E_INVALID): 1 reproduces tidar_reject_sample
+ * bit for bit (the AR logits are used as they are), 0 uses the diffusion
+ * logits as the targets (every in-range draft is then accepted). Each mixed
+ * logit is formed in fp32 as fmaf(trust_ar, a, (1 - trust_ar) * d).
+ * Arguments, layouts, ownership, workspace (tidar_reject_workspace_bytes)
+ * and errors are those of tidar_reject_sample; ratio holds the mixed
+ * p_i(d) / q_i(d).
+ * ---------------------------------------------------------------------- */
+int tidar_reject_sample_trust(int32_t batch, int32_t k, int32_t vocab, const float* ar_logits,
+                              const float* diff_logits, const int32_t* drafts, const float* uniforms,
+                              float temperature, float trust_ar, int32_t* accept_len,
+                              int32_t* next_token, float* ratio, int32_t* dev_status, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

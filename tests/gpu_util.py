@@ -58,7 +58,7 @@ def oracle_inputs(case, layer=0):
 NEAR = 1e-5  # near-tie band of the sampler comparison (fraction of the total mass / of the accept probability)
 
 
-def draw_candidates(ar_logits, diff_logits, b, n, u_last, temperature=1.0, eps=NEAR):
+def draw_candidates(ar_logits, diff_logits, b, n, u_last, temperature=1.0, eps=NEAR, trust_ar=1.0):
     """Tokens whose inverse-CDF interval meets [target - eps*total, target + eps*total].
 
     For a draw the oracle flags as a near-tie, the GPU's token must be one of
@@ -68,7 +68,8 @@ def draw_candidates(ar_logits, diff_logits, b, n, u_last, temperature=1.0, eps=N
     import oracle
 
     k = ar_logits.shape[1] - 1
-    p = oracle.softmax_t(ar_logits[b, n], temperature)
+    p = oracle.softmax_t(oracle.target_logits(ar_logits[b, n], diff_logits[b, n] if n < k else None, trust_ar),
+                         temperature)
     if n < k:
         w = np.maximum(0.0, p - oracle.softmax_t(diff_logits[b, n], temperature))
         if w.sum() == 0.0:
@@ -82,7 +83,7 @@ def draw_candidates(ar_logits, diff_logits, b, n, u_last, temperature=1.0, eps=N
     return np.nonzero((cs > target - eps * total) & (lo < target + eps * total) & (w > 0))[0]
 
 
-def check_samples(ref, acc, nxt, ar_logits, diff_logits, uniforms, temperature=1.0):
+def check_samples(ref, acc, nxt, ar_logits, diff_logits, uniforms, temperature=1.0, trust_ar=1.0):
     """Compare GPU (accept_len, next_token) with the oracle's SampleResult.
 
     Accept lengths must match unless an acceptance test the oracle consulted
@@ -100,7 +101,8 @@ def check_samples(ref, acc, nxt, ar_logits, diff_logits, uniforms, temperature=1
         assert acc[b] == ref.accept_len[b], (b, int(acc[b]), int(ref.accept_len[b]))
         if ref.draw_margin[b] < NEAR:
             draw_near += 1
-            cand = draw_candidates(ar_logits, diff_logits, b, int(acc[b]), uniforms[b, k], temperature)
+            cand = draw_candidates(ar_logits, diff_logits, b, int(acc[b]), uniforms[b, k], temperature,
+                                   trust_ar=trust_ar)
             assert nxt[b] in cand, (b, int(nxt[b]), cand[:8])
         else:
             assert nxt[b] == ref.next_token[b], (b, int(nxt[b]), int(ref.next_token[b]))

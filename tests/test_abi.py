@@ -119,3 +119,11 @@ def test_reject_rejects_bad_arguments():
     assert call(ar=FAKE + 4) == _lib.TIDAR_E_INVALID
     need = lib.tidar_reject_workspace_bytes(1, 16, 151936)
     assert need > 0 and call(wsb=need - 1) == _lib.TIDAR_E_WORKSPACE
+
+
+@pytest.mark.parametrize("lam", [-0.25, 1.5, float("nan"), float("inf")])
+def test_reject_trust_rejects_bad_weight(lam):
+    st = lib.tidar_reject_sample_trust(1, 16, 151936, FAKE, FAKE, FAKE, FAKE, 1.0, lam, FAKE, FAKE, None, None,
+                                       FAKE, 1 << 30, None)
+    assert st == _lib.TIDAR_E_INVALID
+    assert b"trust_ar" in lib.tidar_last_error()

@@ -1,4 +1,5 @@
-"""GPU parity of tidar_reject_sample against the fp64 oracle.
+"""GPU parity of tidar_reject_sample (and its trust-mixing variant,
+tidar_reject_sample_trust) against the fp64 oracle.
 
 Accept lengths and tokens must match bit for bit given the same uniforms.
 Exceptions, counted and printed: a sequence whose consulted acceptance test
@@ -25,7 +26,7 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 NEAR = 1e-5
 
 
-def gpu_reject(ar, diff, drafts, u, temperature=1.0, with_status=False):
+def gpu_reject(ar, diff, drafts, u, temperature=1.0, with_status=False, trust_ar=1.0):
     B, kp1, V = ar.shape
     k = kp1 - 1
     t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, dtype=dt)).cuda()
@@ -40,20 +41,20 @@ def gpu_reject(ar, diff, drafts, u, temperature=1.0, with_status=False):
     ws = torch.empty(tidar.reject_workspace_bytes(B, k, V), dtype=torch.uint8, device="cuda")
     tidar.reject_sample(ar_logits=ar_d, diff_logits=diff_d, drafts=dr_d, uniforms=u_d, accept_len=acc,
                         next_token=nxt, ratio=ratio, dev_status=status, workspace=ws,
-                        temperature=temperature)
+                        temperature=temperature, trust_ar=trust_ar)
     torch.cuda.synchronize()
     res = (acc.cpu().numpy(), nxt.cpu().numpy(), ratio.cpu().numpy())
     return res + (int(status.item()),) if with_status else res
 
 
-def compare(case, name):
+def compare(case, name, trust_ar=1.0):
     ref = oracle.reject_sample(case.ar_logits, case.diff_logits, case.drafts, case.uniforms,
-                               case.temperature)
+                               case.temperature, trust_ar=trust_ar)
     acc, nxt, ratio = gpu_reject(case.ar_logits, case.diff_logits, case.drafts, case.uniforms,
-                                 case.temperature)
+                                 case.temperature, trust_ar=trust_ar)
     mism = (acc != ref.accept_len) | (nxt != ref.next_token)
     excused, draw_near = check_samples(ref, acc, nxt, case.ar_logits, case.diff_logits, case.uniforms,
-                                       case.temperature)
+                                       case.temperature, trust_ar=trust_ar)
     print(f"[parity] {name}: B={case.batch} mismatches={int(mism.sum())} accept near-ties={excused} "
           f"draw near-ties={draw_near} mean accept={ref.accept_len.mean():.2f}", flush=True)
     finite = np.isfinite(ref.ratio)
@@ -65,7 +66,8 @@ def test_golden_hand_examples():
     for c in json.load(open(os.path.join(GOLDEN, "reject_tiny.json")))["cases"]:
         ar = np.log(np.array(c["p"], np.float32))[None]
         diff = np.log(np.array(c["q"], np.float32))[None]
-        acc, nxt, ratio = gpu_reject(ar, diff, np.array([c["drafts"]]), np.array([c["uniforms"]]))
+        acc, nxt, ratio = gpu_reject(ar, diff, np.array([c["drafts"]]), np.array([c["uniforms"]]),
+                                     trust_ar=c.get("trust_ar", 1.0))
         assert acc[0] == c["expect_n"] and nxt[0] == c["expect_c"], c["name"]
         np.testing.assert_allclose(ratio[0], c["ratio"], rtol=1e-5)
 
@@ -128,3 +130,64 @@ def test_bad_draft_id_is_flagged():
     acc, _, _, status = gpu_reject(case.ar_logits, case.diff_logits, drafts, case.uniforms, with_status=True)
     assert status & 16
     assert acc[1] == 0
+
+
+@pytest.mark.parametrize("lam", [0.0, 0.3, 0.5, 0.8])
+def test_trust_mixing_config2(lam):
+    case = config_sampler(2, seed=5, batch=4)
+    ref = compare(case, f"cfg2 V=151936 k=16 trust_ar={lam}", trust_ar=lam)
+    if lam == 0.0:
+        assert (ref.accept_len == 16).all()
+
+
+@pytest.mark.parametrize("lam", [0.25, 0.6])
+def test_trust_mixing_many_sequences(lam):
+    case = sampler_case(batch=256, k=6, vocab=3001, ar_sigma=2.5, diff_mode="noisy", diff_sigma=1.5, seed=13,
+                        temperature=0.8)
+    compare(case, f"V=3001 k=6 T=0.8 trust_ar={lam}", trust_ar=lam)
+
+
+def test_trust_one_entry_matches_plain_entry():
+    """tidar_reject_sample_trust with weight 1 is the plain sampler, bit for bit."""
+    import ctypes
+    from ar_self_speculative_amd import _lib
+    case = config_sampler(2, seed=6, batch=3)
+    B, kp1, V = case.ar_logits.shape
+    k = kp1 - 1
+    t = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a, dtype=dt)).cuda()
+    ar, diff, dr, u = t(case.ar_logits, np.float32), t(case.diff_logits, np.float32), \
+        t(case.drafts, np.int32), t(case.uniforms, np.float32)
+    ws = torch.empty(tidar.reject_workspace_bytes(B, k, V), dtype=torch.uint8, device="cuda")
+    outs = []
+    for fn in ("plain", "trust"):
+        acc = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+        nxt = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+        ratio = torch.zeros((B, k), dtype=torch.float32, device="cuda")
+        head = (B, k, V, ar.data_ptr(), diff.data_ptr(), dr.data_ptr(), u.data_ptr(), 1.0)
+        tail = (acc.data_ptr(), nxt.data_ptr(), ratio.data_ptr(), None, ws.data_ptr(), ws.numel(), None)
+        st = (_lib._lib.tidar_reject_sample(*head, *tail) if fn == "plain"
+              else _lib._lib.tidar_reject_sample_trust(*head, 1.0, *tail))
+        assert st == 0
+        torch.cuda.synchronize()
+        outs.append((acc.cpu().numpy(), nxt.cpu().numpy(), ratio.cpu().numpy()))
+    for a, b in zip(outs[0], outs[1]):
+        assert np.array_equal(a, b)
+
+
+def test_trust_mixture_law_on_gpu():
+    """lambda = 0.5: first committed token over 10^6 GPU draws follows softmax of the mixed logits."""
+    V, k, N, lam = 16, 2, 1_000_000, 0.5
+    rng = np.random.default_rng(22)
+    ar = rng.normal(0, 2.0, size=(k + 1, V)).astype(np.float32)
+    diff = rng.normal(0, 2.0, size=(k, V)).astype(np.float32)
+    q = sp_softmax(diff.astype(np.float64), axis=-1)
+    target = sp_softmax(lam * ar[:k].astype(np.float64) + (1 - lam) * diff.astype(np.float64), axis=-1)
+    drafts = np.stack([rng.choice(V, size=N, p=q[i]) for i in range(k)], axis=1).astype(np.int32)
+    u = rng.random((N, k + 1), dtype=np.float32)
+    acc, nxt, _ = gpu_reject(np.broadcast_to(ar, (N, k + 1, V)), np.broadcast_to(diff, (N, k, V)), drafts, u,
+                             trust_ar=lam)
+    first = np.where(acc >= 1, drafts[:, 0], nxt)
+    obs = np.bincount(first, minlength=V)
+    chi = stats.chisquare(obs, N * target[0])
+    print(f"[stats] trust 0.5 first-token chi2 p-value {chi.pvalue:.3g}", flush=True)
+    assert chi.pvalue > 1e-3
