@@ -329,9 +329,13 @@ struct Wave {
   static constexpr int LA = 2, LB = 2;
   // There is no branch between the phases: code motion across one would undo
   // the interleaving.
-  template <bool QK, bool NEXT>
+  // With MASK, the next tile's scores are masked between the phases (before
+  // their maxima are taken): keys past nvalid, and for a tile of step keys
+  // (local) the keys outside each row's region.
+  template <bool QK, bool NEXT, bool MASK = false>
   __device__ __forceinline__ void step(const lds_u8* kb_next, const lds_u8* vb_cur, const S& s_cur, S& s_next,
-                                       float sl2) {
+                                       float sl2, bool local = false, int nvalid = kBN, int c_base = 0,
+                                       int lane = 0, const RowRule (*rules)[NQT] = nullptr) {
     float muse[NQT];
 #pragma unroll
     for (int nt = 0; nt < NQT; ++nt) muse[nt] = (m[nt] == kNegInf) ? 0.f : m[nt];
@@ -357,6 +361,12 @@ struct Wave {
 #pragma unroll
       for (int nt = 0; nt < NQT; ++nt) probs(s_cur, nt, (SPS / 2) * j, SPS / 2, muse[nt], sl2, pb);
       __builtin_amdgcn_sched_barrier(0);
+    }
+    if (MASK) {
+      if (local)
+        mask<true>(s_next, lane, nvalid, c_base, *rules);
+      else if (nvalid < kBN)
+        mask<false>(s_next, lane, nvalid, 0, *rules);
     }
     // ---- phase B: slot j = (k-step j/DT, dim tile j%DT) ----
     float mx[NQT];
@@ -471,41 +481,27 @@ __device__ __forceinline__ void main_iter(Wave<D, NQT>& st, lds_u8* __restrict__
 // V[t+1] (into vb_dst) are issued, then the tile step runs on K[t+1]
 // (kb_next) and V[t] (vb_cur). The four buffers are distinct; passing them as
 // restrict pointers lets the compiler see that the reads do not wait for the
-// copies in flight. A next tile that needs a mask (the partial last prefix
-// tile, or step keys under the region rule) takes the non-interleaved path.
+// copies in flight. The next tile's scores are masked between the step's
+// phases when it needs it (the partial last prefix tile, or step keys under
+// the region rule); the loop's last tile (P V only) is peeled by the caller.
 template <int D, int NQT, int WAVES>
 __device__ __forceinline__ void tile_iter(Wave<D, NQT>& st, lds_u8* __restrict__ kb_dst,
                                           const lds_u8* __restrict__ kb_next, const lds_u8* __restrict__ vb_cur,
                                           lds_u8* __restrict__ vb_dst, const TileSeq& seq, int t, int wave, int lane,
                                           const RowRule (&rules)[NQT], float sl2, typename Wave<D, NQT>::S& sA,
                                           typename Wave<D, NQT>::S& sB) {
-  using W = Wave<D, NQT>;
-  const int ntot = seq.count();
-  if (t + 2 < ntot) {
+  // t + 1 < count(): the next tile exists (the caller peels the last tile)
+  if (t + 2 < seq.count()) {
     const TileSrc a = seq.at(t + 2);
     copy_tile<D, WAVES>(make_rsrc(a.k, a.bytes), a.vo, a.row0, a.row_bytes, kb_dst, wave);
   }
-  if (t + 1 >= ntot) {
-    st.template step<false, false>(nullptr, vb_cur, sA, sB, sl2);
-  } else {
-    const TileSrc n = seq.at(t + 1);
-    copy_tile<D, WAVES>(make_rsrc(n.v, n.bytes), n.vo, n.row0, n.row_bytes, vb_dst, wave);
-    if (n.local || n.nvalid < kBN) {
-      st.qk(kb_next, sB);
-      if (n.local)
-        W::template mask<true>(sB, lane, n.nvalid, n.c_base, rules);
-      else
-        W::template mask<false>(sB, lane, n.nvalid, 0, rules);
-      st.template step<false, false>(nullptr, vb_cur, sA, sB, sl2);
-      st.tile_max(sB, sl2);
-    } else {
-      st.template step<true, true>(kb_next, vb_cur, sA, sB, sl2);
-    }
+  const TileSrc n = seq.at(t + 1);
+  copy_tile<D, WAVES>(make_rsrc(n.v, n.bytes), n.vo, n.row0, n.row_bytes, vb_dst, wave);
+  st.template step<true, true, true>(kb_next, vb_cur, sA, sB, sl2, n.local, n.nvalid, n.c_base, lane, &rules);
 #pragma unroll
-    for (int nt = 0; nt < NQT; ++nt) {
-      sA[nt][0] = sB[nt][0];
-      sA[nt][1] = sB[nt][1];
-    }
+  for (int nt = 0; nt < NQT; ++nt) {
+    sA[nt][0] = sB[nt][0];
+    sA[nt][1] = sB[nt][1];
   }
   wait_copies();
 }
@@ -650,11 +646,15 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
     main_iter<D, NQT, WAVES>(st, par ? KB[1] : KB[0], par ? KB[0] : KB[1], par ? VB[1] : VB[0],
                              par ? VB[0] : VB[1], seq, t, wave, sl2, sA, sB);
   }
-  for (; t < ntot; ++t) {
+  for (; t + 1 < ntot; ++t) {
     const int par = t & 1;
     __syncthreads();
     tile_iter<D, NQT, WAVES>(st, par ? KB[1] : KB[0], par ? KB[0] : KB[1], par ? VB[1] : VB[0],
                              par ? VB[0] : VB[1], seq, t, wave, lane, rules, sl2, sA, sB);
+  }
+  if (t < ntot) {  // the last tile: P V only (its V is in VB[t & 1])
+    __syncthreads();
+    st.template step<false, false>(nullptr, (t & 1) ? VB[1] : VB[0], sA, sB, sl2);
   }
 
   // o[nt][dt][v] holds O^T[d = 32*dt + 8*(v/4) + 4*half + v%4][this lane's row].
