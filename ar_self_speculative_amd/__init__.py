@@ -6,13 +6,14 @@ Importing it without the built library raises ImportError.
 """
 from ._lib import (  # noqa: F401
     AttnDesc, TidarError, attn_step, attn_workspace, attn_workspace_bytes, kv_commit, last_error, load,
-    make_attn_desc, reject_sample, reject_workspace_bytes, DTYPE_BF16, DTYPE_F32, EXPORTS,
-    LIB_PATH,
+    make_attn_desc, reject_sample, reject_workspace_bytes, token_logprobs, logprob_workspace_bytes,
+    DTYPE_BF16, DTYPE_F32, EXPORTS, LIB_PATH,
 )
 from .step import DecodeStep  # noqa: F401
 
 __all__ = [
     "AttnDesc", "TidarError", "attn_step", "attn_workspace", "attn_workspace_bytes", "kv_commit", "last_error",
-    "make_attn_desc", "reject_sample", "reject_workspace_bytes", "DecodeStep", "DTYPE_BF16",
+    "make_attn_desc", "reject_sample", "reject_workspace_bytes", "token_logprobs", "logprob_workspace_bytes",
+    "DecodeStep", "DTYPE_BF16",
     "DTYPE_F32", "EXPORTS", "LIB_PATH",
 ]

@@ -30,11 +30,13 @@ DEV_ACCEPT_RANGE = 2
 DEV_CAPACITY = 4
 DEV_NONFINITE_ROW = 8
 DEV_DRAFT_RANGE = 16
+DEV_TARGET_RANGE = 32
 
 EXPORTS = (
     "tidar_status_string", "tidar_last_error", "tidar_version",
     "tidar_attn_workspace_bytes", "tidar_attn_step", "tidar_kv_commit",
     "tidar_reject_workspace_bytes", "tidar_reject_sample", "tidar_reject_sample_trust",
+    "tidar_logprob_workspace_bytes", "tidar_token_logprobs",
 )
 
 
@@ -74,6 +76,10 @@ def load() -> ctypes.CDLL:
     lib.tidar_reject_workspace_bytes.argtypes = [i32, i32, i32]
     lib.tidar_reject_sample.restype = ctypes.c_int
     lib.tidar_reject_sample.argtypes = [i32, i32, i32, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, vp, sz, vp]
+    lib.tidar_logprob_workspace_bytes.restype = sz
+    lib.tidar_logprob_workspace_bytes.argtypes = [i32, i32]
+    lib.tidar_token_logprobs.restype = ctypes.c_int
+    lib.tidar_token_logprobs.argtypes = [i32, i32, vp, vp, vp, vp, vp, sz, vp]
     lib.tidar_reject_sample_trust.restype = ctypes.c_int
     lib.tidar_reject_sample_trust.argtypes = [i32, i32, i32, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float,
                                               vp, vp, vp, vp, vp, sz, vp]
@@ -204,3 +210,23 @@ def reject_sample(*, ar_logits, diff_logits, drafts, uniforms, accept_len, next_
     else:
         _check(_lib.tidar_reject_sample_trust(B, k, V, _ptr(ar_logits), _ptr(diff_logits), _ptr(drafts),
                                               _ptr(uniforms), float(temperature), float(trust_ar), *args))
+
+
+def logprob_workspace_bytes(rows: int, vocab: int) -> int:
+    return int(_lib.tidar_logprob_workspace_bytes(rows, vocab))
+
+
+def token_logprobs(*, logits, targets, logprobs, workspace, dev_status=None, stream=None):
+    """Likelihood mode: logprobs[..] = log softmax(logits[.., :])[targets[..]] (one launch pair)."""
+    V = logits.shape[-1]
+    rows = targets.numel()
+    _dev(logits, torch.float32, "logits")
+    _dev(targets, torch.int32, "targets")
+    _dev(logprobs, torch.float32, "logprobs")
+    _dev(dev_status, torch.int32, "dev_status", allow_none=True)
+    _dev(workspace, None, "workspace")
+    if logits.numel() != rows * V or logprobs.numel() != rows:
+        raise ValueError("logits must hold targets.numel() rows of V logits, logprobs one value per row")
+    _check(_lib.tidar_token_logprobs(rows, V, _ptr(logits), _ptr(targets), _ptr(logprobs), _ptr(dev_status),
+                                     _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream(stream)))

@@ -263,4 +263,36 @@ int tidar_reject_sample_trust(int32_t batch, int32_t k, int32_t vocab, const flo
   return TIDAR_OK;
 }
 
+
+size_t tidar_logprob_workspace_bytes(int32_t rows, int32_t vocab) {
+  if (rows < 1 || vocab < 1) return 0;
+  return tidar::logprob_workspace_bytes(rows, vocab);
+}
+
+int tidar_token_logprobs(int32_t rows, int32_t vocab, const float* logits, const int32_t* targets, float* logprobs,
+                         int32_t* dev_status, void* workspace, size_t workspace_bytes, void* stream) {
+  if (rows < 1 || vocab < 1) return fail(TIDAR_E_INVALID, "need rows >= 1 and vocab >= 1");
+  const long nchunks = (vocab + tidar::logprob_chunk() - 1) / tidar::logprob_chunk();
+  if ((long)rows * vocab > 0x7fffffffL || (long)rows * nchunks > 0x7fffffffL)
+    return fail(TIDAR_E_UNSUPPORTED, "logits too large");
+  if (!logits || !targets || !logprobs) return fail(TIDAR_E_INVALID, "a required pointer is NULL");
+  if (!aligned(logits, 16)) return fail(TIDAR_E_INVALID, "logits must be 16-byte aligned");
+  const size_t need = tidar::logprob_workspace_bytes(rows, vocab);
+  if (!workspace || workspace_bytes < need)
+    return fail(TIDAR_E_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
+  if (!aligned(workspace, 256)) return fail(TIDAR_E_INVALID, "workspace must be 256-byte aligned");
+  tidar::LogprobParams p{};
+  p.rows = rows;
+  p.V = vocab;
+  p.nchunks = (int)nchunks;
+  p.logits = logits;
+  p.targets = targets;
+  p.logprobs = logprobs;
+  p.dev_status = dev_status;
+  p.stats = static_cast<float2*>(workspace);
+  hipError_t e = tidar::launch_logprob(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "logprob launch");
+  return TIDAR_OK;
+}
+
 }  // extern "C"

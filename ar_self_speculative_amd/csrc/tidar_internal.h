@@ -86,4 +86,16 @@ int reject_max_chunks();
 void plan_reject(RejectParams& p);
 hipError_t launch_reject(const RejectParams& p, hipStream_t stream);
 
+struct LogprobParams {
+  int rows, V, nchunks;
+  const float* logits;     // [rows, V]
+  const int32_t* targets;  // [rows]
+  float* logprobs;         // [rows]
+  int32_t* dev_status;
+  float2* stats;           // [rows, nchunks] (max, sum exp) per vocabulary chunk
+};
+size_t logprob_workspace_bytes(int rows, int V);
+int logprob_chunk();
+hipError_t launch_logprob(const LogprobParams& p, hipStream_t stream);
+
 }  // namespace tidar

@@ -114,6 +114,159 @@ def cpu_baseline(seconds: float = 8.0) -> dict:
                        f"call at V=151936 k=16 ({t_samp:.2f} s), one 36-layer commit ({t_commit:.3f} s)")}
 
 
+def _rand_bf16(shape, gen):
+    import torch
+
+    return torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+
+
+def _time_graph(g, reps: int) -> float:
+    """Milliseconds per replay of graph g (HIP events on the launch stream)."""
+    import torch
+
+    g.replay()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / reps
+
+
+def _capture(fn):
+    import torch
+
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def likelihood_bench(args) -> None:
+    """Likelihood mode: one causal forward scoring R tokens after a prefix P
+    (36 attention layers with num_blocks = 0, then the log-probabilities of
+    the R next tokens over the vocabulary)."""
+    import math
+
+    import torch
+
+    import ar_self_speculative_amd as tidar
+
+    s = SHAPE
+    L, Hq, Hkv, D, P, V = s["layers"], s["num_q_heads"], s["num_kv_heads"], s["head_dim"], s["P"], s["vocab"]
+    R = args.likelihood
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    desc = tidar.make_attn_desc(batch=1, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, k=R, num_blocks=0,
+                                block_len=1, cache_capacity=P + R, max_cache_len=P, sm_scale=1 / math.sqrt(D),
+                                dtype=tidar.DTYPE_BF16)
+    q = _rand_bf16((L, 1, R, Hq, D), gen)
+    ks, vs = _rand_bf16((L, 1, R, Hkv, D), gen), _rand_bf16((L, 1, R, Hkv, D), gen)
+    kc, vc = _rand_bf16((L, 1, Hkv, P + R, D), gen), _rand_bf16((L, 1, Hkv, P + R, D), gen)
+    lens = torch.full((1,), P, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = tidar.attn_workspace(desc, torch.device("cuda"))
+    logits = torch.randn((R, V), generator=gen, device="cuda", dtype=torch.float32) * 3.0
+    targets = torch.randint(0, V, (R,), generator=gen, device="cuda", dtype=torch.int32)
+    lp = torch.empty(R, dtype=torch.float32, device="cuda")
+    lws = torch.empty(tidar.logprob_workspace_bytes(R, V), dtype=torch.uint8, device="cuda")
+
+    def attention():
+        for l in range(L):
+            tidar.attn_step(desc, q[l], ks[l], vs[l], kc[l], vc[l], lens, out[l], None, status, ws)
+
+    def scores():
+        tidar.token_logprobs(logits=logits, targets=targets, logprobs=lp, workspace=lws, dev_status=status)
+
+    for _ in range(args.warmup):
+        attention()
+        scores()
+    g_all = _capture(lambda: (attention(), scores()))
+    g_lp = _capture(scores)
+    ms = _time_graph(g_all, args.steps)
+    ms_lp = _time_graph(g_lp, args.steps)
+    if int(status.item()):
+        print(f"device status flags set: {int(status.item())}", file=sys.stderr)
+        sys.exit(1)
+    lp_gbps = R * V * 4 / (ms_lp * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": f"likelihood-mode scored tokens/s (one causal forward: {L} attention layers + log-probs) "
+                  f"at P={P},R={R}",
+        "value": round(R / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_forward": round(ms, 4), "higher_is_better": True, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"qwen3-8b-shape causal scoring forward, batch 1, prefix {P}, {R} scored tokens, "
+                               f"vocab {V}", "layers": L, "prefix": P, "rows": R, "vocab": V},
+        "logprob_us": round(ms_lp * 1e3, 2),
+        "logprob_roofline": {"bound": "hbm", "achieved": round(lp_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                             "frac": round(lp_gbps / HBM_PEAK_GBPS, 4), "bytes_per_launch": R * V * 4},
+    }), flush=True)
+
+
+def knee_bench(args) -> None:
+    """Append-prefill sweep (one layer, 64 query heads, 8 KV heads, head_dim
+    128): attention time per launch for each prefix P and row count R, the
+    knee where more rows stop being nearly free, and the largest draft length
+    k whose hybrid step (k + (k+1)k rows) fits under it."""
+    import math
+
+    import torch
+
+    import ar_self_speculative_amd as tidar
+
+    Hq, Hkv, D = 64, 8, 128
+    Ps, Rs = (512, 1024, 2048, 4096), (1, 8, 16, 32, 64, 128, 256, 512)
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    nbuf = 32  # distinct caches per timed graph (32 x 16.8 MB at P=4096 > the 256 MB last-level cache)
+    table = {}
+    for P in Ps:
+        kcs = [_rand_bf16((1, Hkv, P + 512, D), gen) for _ in range(nbuf)]
+        vcs = [_rand_bf16((1, Hkv, P + 512, D), gen) for _ in range(nbuf)]
+        lens = torch.full((1,), P, dtype=torch.int32, device="cuda")
+        for R in Rs:
+            desc = tidar.make_attn_desc(batch=1, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, k=R, num_blocks=0,
+                                        block_len=1, cache_capacity=P + 512, max_cache_len=P,
+                                        sm_scale=1 / math.sqrt(D), dtype=tidar.DTYPE_BF16)
+            q = _rand_bf16((1, R, Hq, D), gen)
+            ks, vs = _rand_bf16((1, R, Hkv, D), gen), _rand_bf16((1, R, Hkv, D), gen)
+            out = torch.empty_like(q)
+            ws = tidar.attn_workspace(desc, torch.device("cuda"))
+
+            def run():
+                for i in range(nbuf):
+                    tidar.attn_step(desc, q, ks, vs, kcs[i], vcs[i], lens, out, None, None, ws)
+
+            run()
+            g = _capture(run)
+            table[(P, R)] = _time_graph(g, 3) * 1e3 / nbuf
+    knee = {}
+    for P in Ps:
+        base = table[(P, 1)]
+        knee[P] = max(R for R in Rs if table[(P, R)] <= 1.25 * base)
+    g = Hq // Hkv
+    # packed query rows (rows x group) at the knee; the Qwen3-8B decode step
+    # packs k + (k+1)k rows x 4 query heads per KV head
+    packed = knee[4096] * g
+    g_step = SHAPE["num_q_heads"] // SHAPE["num_kv_heads"]
+    k_pick = max([k for k in (1, 2, 4, 8, 16) if (k + (k + 1) * k) * g_step <= packed] or [1])
+    print(json.dumps({
+        "metric": "append-prefill attention us per launch (64 q heads, 8 kv heads, d 128) and its knee",
+        "unit": "us", "n_gpus": 1, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "one layer, batch 1, append-prefill sweep", "P": list(Ps), "R": list(Rs),
+                   "caches_rotated": nbuf},
+        "us": {str(P): [round(table[(P, R)], 2) for R in Rs] for P in Ps},
+        "knee_rule": "largest R with time <= 1.25 x time at R = 1",
+        "knee_R": {str(P): knee[P] for P in Ps},
+        "knee_rows_times_group": {str(P): knee[P] * g for P in Ps},
+        "draft_length_at_P4096": {"rule": "largest k whose step packs at most the knee's rows x group",
+                                  "k": k_pick, "rows": k_pick + (k_pick + 1) * k_pick,
+                                  "packed_rows": (k_pick + (k_pick + 1) * k_pick) * g_step},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -123,6 +276,10 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="force the prefix split count (0 = library plan)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run three device copies of MIB MiB (counter calibration) and exit")
+    ap.add_argument("--likelihood", type=int, default=0, metavar="R",
+                    help="only time likelihood mode: one causal forward scoring R tokens (P=4096), and exit")
+    ap.add_argument("--knee", action="store_true",
+                    help="only run the append-prefill sweep, report its knee and the draft length it allows")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the hot path is measured on a "
@@ -131,6 +288,12 @@ def main():
 
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.likelihood:
+        likelihood_bench(args)
+        return
+    if args.knee:
+        knee_bench(args)
         return
 
     import torch

@@ -62,7 +62,8 @@ enum {
   TIDAR_DEV_ACCEPT_RANGE = 2,      /* accept_len[b] outside 0..k: sequence not committed */
   TIDAR_DEV_CAPACITY = 4,          /* cache_len_in[b] + n > cache_capacity: not committed */
   TIDAR_DEV_NONFINITE_ROW = 8,     /* a logit row had no finite maximum or a zero sum */
-  TIDAR_DEV_DRAFT_RANGE = 16       /* a draft token id outside 0..V-1: treated as rejected */
+  TIDAR_DEV_DRAFT_RANGE = 16,      /* a draft token id outside 0..V-1: treated as rejected */
+  TIDAR_DEV_TARGET_RANGE = 32      /* a likelihood target id outside 0..V-1: its score is NaN */
 };
 
 const char* tidar_status_string(int status);
@@ -203,6 +204,34 @@ int tidar_reject_sample_trust(int32_t batch, int32_t k, int32_t vocab, const flo
                               float temperature, float trust_ar, int32_t* accept_len,
                               int32_t* next_token, float* ratio, int32_t* dev_status, void* workspace,
                               size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Likelihood mode: per-token AR log-probabilities (talk notes on
+ * notes.yuuk.io, 尤度評価: with the attention mask set to causal, TiDAR
+ * scores a sequence as an AR model in one forward, no Monte-Carlo sampling;
+ * review, 实验与结果: one NFE with a pure causal mask). The causal forward
+ * is tidar_attn_step with num_blocks = 0 (append-prefill rows, causal among
+ * themselves over the full prefix); this call turns the resulting logits
+ * into scores:
+ *   logprobs[r] = logits[r, targets[r]] - log(sum_v exp(logits[r, v]))
+ * (temperature 1; fp32 statistics per 4096-token chunk merged in a fixed
+ * order, so results are run-to-run deterministic).
+ *
+ * logits [rows, V] f32 (e.g. [B, R, V] flattened; 16-byte aligned),
+ * targets [rows] int32 (the next token of each row), logprobs [rows] f32
+ * output. A target outside 0..V-1 scores NaN and sets
+ * TIDAR_DEV_TARGET_RANGE; a row with no finite maximum or a zero sum scores
+ * NaN and sets TIDAR_DEV_NONFINITE_ROW. Workspace: at least
+ * tidar_logprob_workspace_bytes(rows, V) bytes, 256-byte aligned (0 is
+ * returned for rows < 1 or V < 1). Errors: TIDAR_E_INVALID (shape, NULL,
+ * alignment), TIDAR_E_UNSUPPORTED (rows * V >= 2^31), TIDAR_E_WORKSPACE,
+ * TIDAR_E_HIP.
+ * ---------------------------------------------------------------------- */
+size_t tidar_logprob_workspace_bytes(int32_t rows, int32_t vocab);
+
+int tidar_token_logprobs(int32_t rows, int32_t vocab, const float* logits, const int32_t* targets,
+                         float* logprobs, int32_t* dev_status, void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 #ifdef __cplusplus
 }

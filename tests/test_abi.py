@@ -127,3 +127,20 @@ def test_reject_trust_rejects_bad_weight(lam):
                                        FAKE, 1 << 30, None)
     assert st == _lib.TIDAR_E_INVALID
     assert b"trust_ar" in lib.tidar_last_error()
+
+
+def test_logprob_rejects_bad_arguments():
+    def call(**kw):
+        a = dict(rows=4, V=151936, lg=FAKE, tg=FAKE, out=FAKE, ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return lib.tidar_token_logprobs(a["rows"], a["V"], a["lg"], a["tg"], a["out"], None, a["ws"], a["wsb"], None)
+    assert call(rows=0) == _lib.TIDAR_E_INVALID
+    assert call(V=0) == _lib.TIDAR_E_INVALID
+    assert call(lg=None) == _lib.TIDAR_E_INVALID
+    assert call(tg=None) == _lib.TIDAR_E_INVALID
+    assert call(lg=FAKE + 4) == _lib.TIDAR_E_INVALID
+    assert call(rows=1 << 20) == _lib.TIDAR_E_UNSUPPORTED
+    need = lib.tidar_logprob_workspace_bytes(4, 151936)
+    assert need >= 4 * 38 * 8 and call(wsb=need - 1) == _lib.TIDAR_E_WORKSPACE
+    assert call(ws=FAKE + 16) == _lib.TIDAR_E_INVALID
+    assert lib.tidar_logprob_workspace_bytes(0, 10) == 0
