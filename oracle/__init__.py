@@ -19,6 +19,8 @@ Contents (every function cites the passage it follows):
 * ``commit.kv_commit``      - exact-KV append of accepted drafts.
 * ``likelihood.token_logprobs`` - AR log-likelihood of each next token from
   the logits of the causal (likelihood-mode) forward.
+* ``loop``                  - the step loop around the path: rows and
+  positions of a step, and how verification picks the next step's inputs.
 
 All floating point is fp64. Pins live in ``tests/test_oracle_*.py``; no part
 is "parity unpinned".
@@ -28,10 +30,11 @@ from .dense import attn_dense, hybrid_mask_matrix
 from .reject import reject_sample, invcdf, softmax_t, SampleResult, selected_block_rows, target_logits
 from .commit import kv_commit
 from .likelihood import token_logprobs, sequence_loglik, log_normaliser
+from . import loop
 
 __all__ = [
     "attn_step", "attn_rows", "local_keys", "visible_local_count", "attn_dense",
     "hybrid_mask_matrix", "reject_sample", "invcdf", "softmax_t",
     "SampleResult", "selected_block_rows", "target_logits", "kv_commit",
-    "token_logprobs", "sequence_loglik", "log_normaliser",
+    "token_logprobs", "sequence_loglik", "log_normaliser", "loop",
 ]
