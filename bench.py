@@ -267,6 +267,76 @@ def knee_bench(args) -> None:
     }), flush=True)
 
 
+def loop_bench(args) -> None:
+    """The TiDAR step loop with a random-weight Qwen3-8B-shaped decoder:
+    time per step (one NFE: 36 layers of GEMMs + hybrid attention, the
+    sampler, the commit and the next drafts), tokens per NFE, and the share of
+    the step spent in the hybrid attention."""
+    import torch
+
+    import ar_self_speculative_amd as tidar
+    from ar_self_speculative_amd.loop import TiDARLoop, TinyDecoder
+
+    s = SHAPE
+    L, Hq, Hkv, D, P, V, k = s["layers"], s["num_q_heads"], s["num_kv_heads"], s["head_dim"], s["P"], s["vocab"], \
+        s["k"]
+    model = TinyDecoder(vocab=V, hidden=4096, layers=L, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, mlp=12288,
+                        seed=0)
+    cap = P + 2048
+    lp = TiDARLoop(model, batch=1, k=k, cache_capacity=cap)
+    gen = torch.Generator(device="cuda").manual_seed(1)
+    lp.k_cache.copy_(torch.randn(lp.k_cache.shape, generator=gen, device="cuda").to(torch.bfloat16))
+    lp.v_cache.copy_(torch.randn(lp.v_cache.shape, generator=gen, device="cuda").to(torch.bfloat16))
+    lp.region.copy_(torch.randint(0, V - 1, lp.region.shape, generator=gen, device="cuda", dtype=torch.int32))
+    lp.q_logits.zero_()
+    uv = torch.rand((1, k), generator=gen, device="cuda")
+    ud = torch.rand((1, k - 1), generator=gen, device="cuda")
+    emitted = torch.zeros(1, dtype=torch.int64, device="cuda")
+
+    def one_step():
+        lp.step(uv, ud)
+        emitted.add_(lp.accept_len.long() + 1)
+
+    lp.cache_len.fill_(P)
+    for _ in range(args.warmup):
+        one_step()
+    lp.cache_len.fill_(P)
+    g = _capture(one_step)
+    reps = args.steps
+    if P + (reps + 2) * k > cap - k:
+        reps = (cap - k - P) // k - 2
+    lp.cache_len.fill_(P)
+    emitted.zero_()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    tokens_per_nfe = int(emitted.item()) / reps
+    # the hybrid attention alone, on the same buffers and prefix length
+    lp.cache_len.fill_(P)
+    ga = _capture(lambda: [tidar.attn_step(lp.desc, lp.last_q, lp.k_step[l], lp.v_step[l], lp.k_cache[l],
+                                           lp.v_cache[l], lp.cache_len, lp.attn_out, None, lp.status, lp.attn_ws)
+                           for l in range(L)])
+    ms_attn = _time_graph(ga, 5)
+    if int(lp.status.item()):
+        print(f"device status flags set: {int(lp.status.item())}", file=sys.stderr)
+        sys.exit(1)
+    print(json.dumps({
+        "metric": "TiDAR step loop NFE/s with a random-weight Qwen3-8B-shape decoder (k=16 region rows, P~4096)",
+        "value": round(1e3 / ms, 2), "unit": "NFE/s", "n_gpus": 1, "steps": reps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": "bf16", "data": "synthetic, random weights",
+        "config": {"workload": "qwen3-8b-shape decoder (hidden 4096, 36 layers, 32/8 heads, head_dim 128, "
+                               "MLP 12288, vocab 151936), batch 1, prefix 4096, k=16 region rows (288 rows)",
+                   "layers": L, "prefix": P, "k": k, "rows": lp.R},
+        "tokens_per_nfe": round(tokens_per_nfe, 3),
+        "attention_ms_per_step": round(ms_attn, 4),
+        "attention_share": round(ms_attn / ms, 4),
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -278,6 +348,8 @@ def main():
                     help="only run three device copies of MIB MiB (counter calibration) and exit")
     ap.add_argument("--likelihood", type=int, default=0, metavar="R",
                     help="only time likelihood mode: one causal forward scoring R tokens (P=4096), and exit")
+    ap.add_argument("--loop", action="store_true",
+                    help="only time the TiDAR step loop with a random-weight Qwen3-8B-shaped decoder, and exit")
     ap.add_argument("--knee", action="store_true",
                     help="only run the append-prefill sweep, report its knee and the draft length it allows")
     args = ap.parse_args()
@@ -294,6 +366,9 @@ def main():
         return
     if args.knee:
         knee_bench(args)
+        return
+    if args.loop:
+        loop_bench(args)
         return
 
     import torch
