@@ -239,17 +239,24 @@ struct Wave {
   // S^T = K Q^T for one tile, not interleaved (first tile and step keys).
   // s[nt][mt][v] is the score of key 32*mt + 8*(v/4) + 4*half + (v%4).
   __device__ __forceinline__ void qk(const lds_u8* kb, S& s) const {
+    // Standalone S^T = K Q^T (tiles that are not interleaved with a step):
+    // the K fragments are read QLA MFMA slots ahead so the LDS latency
+    // overlaps the matrix work.
+    constexpr int N = 2 * DSTEPS, QLA = 4;
 #pragma unroll
     for (int nt = 0; nt < NQT; ++nt) s[nt][0] = s[nt][1] = f32x16{};
+    bf16x8 a[N];
 #pragma unroll
-    for (int st = 0; st < DSTEPS; ++st)
+    for (int j = 0; j < QLA; ++j) a[j] = kfrag(kb, j >> 1, j & 1);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 a = kfrag(kb, st, mt);
+    for (int j = 0; j < N; ++j) {
+      if (j + QLA < N) a[j + QLA] = kfrag(kb, (j + QLA) >> 1, (j + QLA) & 1);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int nt = 0; nt < NQT; ++nt)
-          s[nt][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[nt][st], s[nt][mt], 0, 0, 0);
-      }
+      for (int nt = 0; nt < NQT; ++nt)
+        s[nt][j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j], qf[nt][j >> 1], s[nt][j & 1], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   // keys at tile positions >= nvalid, or (step keys) outside the row's region, get -inf
@@ -536,16 +543,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
   const int kvh = w % p.Hkv;
   const int b = w / p.Hkv;
 
-  int len = __builtin_amdgcn_readfirstlane(p.cache_len[b]);  // uniform: keeps the tile loop scalar
-  if (len < 0 || len > p.max_len) {
-    if (tid == 0 && p.dev_status) atomicOr(p.dev_status, 1);
-    len = min(max(len, 0), p.max_len);
-  }
-  const bool last = (s == p.S - 1);
-  const int kbeg = s * p.chunk;
-  const int kend = last ? len : min(kbeg + p.chunk, len);
-  const int nk = max(0, kend - kbeg);
-
+  // Q first: its loads do not depend on the cache length, so they are in
+  // flight while the length is fetched. Rows past M load row 0 (in bounds)
+  // and are zeroed, which keeps the eight loads free of branches.
   const int M = p.R * p.g;
   W st;
   st.init_addr(lane);
@@ -559,13 +559,26 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
     rules[nt] = row_rule(r, p.k, p.block_len);
     const u16* qp = reinterpret_cast<const u16*>(p.q) + ((size_t)(b * p.R + r) * p.Hq + h) * D + 8 * half;
 #pragma unroll
-    for (int i = 0; i < DSTEPS; ++i)
-      st.qf[nt][i] = ok ? *reinterpret_cast<const bf16x8*>(qp + 16 * i) : bf16x8{};
+    for (int i = 0; i < DSTEPS; ++i) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + 16 * i);
+      st.qf[nt][i] = ok ? v : bf16x8{};
+    }
 #pragma unroll
     for (int i = 0; i < DT; ++i) st.o[nt][i] = f32x16{};
     st.m[nt] = kNegInf;
     st.l[nt] = 0.f;
   }
+
+  int len = __builtin_amdgcn_readfirstlane(p.cache_len[b]);  // uniform: keeps the tile loop scalar
+  if (len < 0 || len > p.max_len) {
+    if (tid == 0 && p.dev_status) atomicOr(p.dev_status, 1);
+    len = min(max(len, 0), p.max_len);
+  }
+  const bool last = (s == p.S - 1);
+  const int kbeg = s * p.chunk;
+  const int kend = last ? len : min(kbeg + p.chunk, len);
+  const int nk = max(0, kend - kbeg);
+
   const float sl2 = p.scale_log2;
 
   // ---- the tile sequence: prefix keys [kbeg, kend), then (last split only)
