@@ -65,8 +65,12 @@ int check_desc(const tidar_attn_desc* d, tidar::AttnPlan* plan) {
   const long qe = (long)d->batch * R * d->num_q_heads * D;
   const long ce = (long)d->batch * d->num_kv_heads * (long)d->cache_capacity * D;
   if (qe > kMaxElems || ce > kMaxElems) return fail(TIDAR_E_UNSUPPORTED, "tensor too large for 32-bit indexing");
+  // 64-key tiles of step keys a query tile may see: the whole causal run in
+  // append-prefill mode, else the drafts plus one block
+  const int local_tiles = d->num_blocks == 0 ? (int)((R + 63) / 64)
+                                             : (d->k + 63) / 64 + (d->block_len + 63) / 64;
   *plan = tidar::plan_attn(d->dtype, d->batch, d->num_q_heads, d->num_kv_heads, D, (int)R, d->max_cache_len,
-                           d->num_splits);
+                           d->num_splits, local_tiles);
   return TIDAR_OK;
 }
 

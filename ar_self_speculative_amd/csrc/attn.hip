@@ -944,7 +944,8 @@ hipError_t launch_merge(const AttnParams& p, bool bf16, hipStream_t stream) {
 
 }  // namespace
 
-AttnPlan plan_attn(int dtype, int B, int Hq, int Hkv, int D, int R, int max_len, int forced_splits) {
+AttnPlan plan_attn(int dtype, int B, int Hq, int Hkv, int D, int R, int max_len, int forced_splits,
+                   int local_tiles) {
   AttnPlan pl{};
   const int g = Hq / Hkv;
   const long M = (long)R * g;
@@ -964,14 +965,46 @@ AttnPlan plan_attn(int dtype, int B, int Hq, int Hkv, int D, int R, int max_len,
   }
   const int ntiles = (max_len + kBN - 1) / kBN;
   int S;
+  const char* target_env = getenv("TIDAR_ATTN_TARGET_WG");
   if (forced_splits > 0) {
     S = forced_splits;
+  } else if (dtype == 1 && !target_env) {
+    // bf16: pick the split count from a cost model in shader cycles whose
+    // constants were measured on this kernel (head_dim 128, MI355X):
+    //  - a workgroup costs F (prologue and epilogue) plus t per 64-key tile;
+    //    t is lower when the workgroup has its CU to itself (at most 256
+    //    workgroups) than when two share it; past 512 the workgroups run in
+    //    further rounds;
+    //  - the split that owns the last prefix keys also has the step's keys;
+    //  - the merge of S > 1 partials costs a fixed part (its launch and the
+    //    kernel boundary), one memory round trip per 8 partials (it folds
+    //    them in rounds of 8) and a part per partial element (~3.3 TB/s).
+    const double F = 16000.0, t1 = 2650.0 * D / 128, t2 = 3300.0 * D / 128;
+    const double part_elems = (double)B * R * Hq * D;
+    double best = 0.0;
+    S = 1;
+    for (int st = 1; st <= std::max(1, std::min(ntiles, 64)); ++st) {
+      const int ch = ntiles > 0 ? (ntiles + st - 1) / st : 1;
+      const int se = ntiles > 0 ? (ntiles + ch - 1) / ch : 1;
+      if (se != st) continue;  // the same plan as a smaller count
+      const long wgs = base * se;
+      const long rounds = (wgs + 511) / 512;
+      const double t = wgs <= 256 ? t1 : t2;
+      const int n_last = ntiles - (se - 1) * ch + local_tiles;
+      const double cost = rounds * (F + std::max(ch, n_last) * t) +
+                          (se > 1 ? 6000.0 + 2500.0 * ((se + 7) / 8) + se * part_elems * 1.26e-3 : 0.0);
+      if (st == 1 || cost < best) {
+        best = cost;
+        S = se;
+      }
+    }
   } else {
     // Fill the resident workgroup slots (two per CU on the 256-CU part) in
     // one round: a second, partial round would cost as much as the first.
-    // Keep at least two key tiles per split.
+    // Keep at least two key tiles per split. TIDAR_ATTN_TARGET_WG sets the
+    // slot count (and selects this rule for bf16 too).
     long slots = 512;
-    if (const char* e = getenv("TIDAR_ATTN_TARGET_WG")) slots = std::max(1L, atol(e));
+    if (target_env) slots = std::max(1L, atol(target_env));
     S = (int)std::max(1L, slots / base);
     S = std::max(1, std::min(S, std::max(1, ntiles / 2)));
   }

@@ -41,7 +41,8 @@ struct AttnPlan {
   size_t ws_bytes;
 };
 
-AttnPlan plan_attn(int dtype, int B, int Hq, int Hkv, int D, int R, int max_len, int forced_splits);
+AttnPlan plan_attn(int dtype, int B, int Hq, int Hkv, int D, int R, int max_len, int forced_splits,
+                   int local_tiles);
 hipError_t launch_attn_bf16(const AttnParams& p, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream);
 
