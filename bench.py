@@ -76,9 +76,10 @@ def copy_calibration(mib: int) -> None:
 
 
 def cpu_baseline(seconds: float = 8.0) -> dict:
-    """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload
+    (all of the host's cores for the BLAS calls, then one core)."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import oracle
     from tidar_synth import commit_accept_lengths, config_attn, config_sampler
@@ -108,7 +109,18 @@ def cpu_baseline(seconds: float = 8.0) -> dict:
     for info in threadpool_info():
         if info.get("internal_api") in ("openblas", "mkl", "blis"):
             threads = max(threads, int(info.get("num_threads", 1)))
+    # the attention rows again with the BLAS pools held to one thread
+    with threadpool_limits(limits=1):
+        rows1, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < seconds / 2 or rows1 < 16:
+            batch = [(0, int(rng.integers(R)), int(rng.integers(Hq))) for _ in range(16)]
+            oracle.attn_rows(c.q[0], c.k_step[0], c.v_step[0], c.k_cache[0], c.v_cache[0], c.cache_len, batch,
+                             k=c.k, num_blocks=c.num_blocks, block_len=c.block_len, sm_scale=c.sm_scale)
+            rows1 += len(batch)
+        t_row1 = (time.perf_counter() - t0) / rows1
+    t_step1 = L * R * Hq * t_row1 + t_samp + t_commit
     return {"value": 1.0 / t_step, "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "value_1core": 1.0 / t_step1,
             "sample": (f"{rows} attention rows (b,r,h) of one Qwen3-8B layer at P=4096 "
                        f"({t_row * 1e3:.2f} ms/row, scaled to 36 layers x {R * Hq} rows), one full sampler "
                        f"call at V=151936 k=16 ({t_samp:.2f} s), one 36-layer commit ({t_commit:.3f} s)")}
@@ -424,6 +436,9 @@ def main():
                              s["P"], s["k"], s["vocab"])
     t_step = ms_step * 1e-3
     kv_bytes = s["layers"] * (cnt["kv_prefix_layer"] + cnt["kv_step_layer"])
+    # every byte the step must move at least once: Q, K/V (prefix and step) and O of every layer, and
+    # the logits the sampler reads (the commit's few MB depend on the accept lengths and are left out)
+    comp_bytes = s["layers"] * cnt["attn_bytes_layer"] + cnt["sampler_bytes"]
     kv_gbps = kv_bytes / t_step / 1e9
     achieved_tflops = cnt["attn_flops_layer"] / (attn_ms * 1e-3) / 1e12
     res = {
@@ -445,6 +460,8 @@ def main():
                    "kv_heads": s["num_kv_heads"], "head_dim": s["head_dim"], "prefix": s["P"], "k": s["k"],
                    "query_rows": cnt["R"], "vocab": s["vocab"]},
         "kv_read_gbps": round(kv_gbps, 1),
+        "compulsory_gbps": round(comp_bytes / t_step / 1e9, 1),
+        "compulsory_frac_of_hbm_peak": round(comp_bytes / t_step / 1e9 / HBM_PEAK_GBPS, 4),
         "kv_read_frac_of_hbm_peak": round(kv_gbps / HBM_PEAK_GBPS, 4),
         "attn_us_per_layer": round(attn_ms * 1e3, 2),
         "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel<128> (+ split merge)",
