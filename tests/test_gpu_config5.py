@@ -1,4 +1,4 @@
-"""Ragged batch, several decode steps end to end (attention -> sampler -> commit).
+"""Ragged batch, 64 decode steps end to end (attention -> sampler -> commit).
 
 Eight sequences with prefix lengths drawn from U{256..4096}, k = 8 (R = 80
 query rows), Qwen3-8B heads (32 query, 8 KV, D = 128), cache capacity 4608,
@@ -6,7 +6,7 @@ two layers of the 36 (every layer runs the same kernels on its own slice).
 Each step draws fresh queries, step keys/values and verifier inputs. The
 oracle keeps its own cache and lengths and is compared after every step:
 
-* attention on sampled rows of every layer (max-abs 2e-2, bf16),
+* attention on sampled rows of every layer, every 8th step (max-abs 2e-2, bf16),
 * accept lengths and next tokens (bit-exact except oracle-flagged near-ties),
 * the committed caches and the new lengths (bit-exact), after which the
   next step attends over the grown prefixes.
@@ -30,10 +30,11 @@ def _bits(t):
     return t.view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+@pytest.mark.timeout(400)
 def test_config5_ragged_multistep():
     import ar_self_speculative_amd as tidar
 
-    L, steps = 2, 3
+    L, steps = 2, 64
     c = config_attn(5, seed=0, layers=L)
     B, k, R, cap = c.batch, c.k, c.rows, c.cache_capacity
     Hq, Hkv, D = c.num_q_heads, c.num_kv_heads, c.head_dim
@@ -72,7 +73,7 @@ def test_config5_ragged_multistep():
         # attention on sampled rows of every layer, against the oracle's own cache
         out = step.out.float().cpu().numpy()
         srng = np.random.default_rng(1000 + it)
-        for layer in range(L):
+        for layer in (range(L) if it % 8 == 0 or it == steps - 1 else ()):
             rows = [(int(srng.integers(B)), int(r), int(srng.integers(Hq)))
                     for r in (0, k - 1, k, k + k - 1, R - 1, *srng.integers(R, size=19))]
             kcf = bf16_bits_to_f32(kc_bits[layer])
@@ -81,7 +82,8 @@ def test_config5_ragged_multistep():
                                       num_blocks=k + 1, block_len=k, sm_scale=c.sm_scale)
             got = np.stack([out[layer, b, r, h] for b, r, h in rows])
             err = float(np.abs(got - ref).max())
-            print(f"[parity] cfg5 step {it} layer {layer}: max-abs {err:.3e}", flush=True)
+            if it % 16 == 0 or it == steps - 1:
+                print(f"[parity] cfg5 step {it} layer {layer}: max-abs {err:.3e}", flush=True)
             assert err <= 2e-2
 
         # sampler

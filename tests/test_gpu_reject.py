@@ -191,3 +191,15 @@ def test_trust_mixture_law_on_gpu():
     chi = stats.chisquare(obs, N * target[0])
     print(f"[stats] trust 0.5 first-token chi2 p-value {chi.pvalue:.3g}", flush=True)
     assert chi.pvalue > 1e-3
+
+
+def test_bitwise_deterministic_over_ten_calls():
+    case = config_sampler(2, seed=9, batch=4)
+    outs = [gpu_reject(case.ar_logits, case.diff_logits, case.drafts, case.uniforms, trust_ar=lam)
+            for lam in (1.0, 0.4) for _ in range(5)]
+    for i in (1, 2, 3, 4):
+        for a, b in zip(outs[0], outs[i]):
+            assert np.array_equal(a, b)
+    for i in (6, 7, 8, 9):
+        for a, b in zip(outs[5], outs[i]):
+            assert np.array_equal(a, b)
