@@ -1,6 +1,7 @@
 // C ABI of libtidar: argument validation, workspace sizing, split planning
 // and kernel launches. Every check runs on the host before any HIP call, so
 // a bad argument never reaches the device.
+#include <limits.h>
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -32,6 +33,12 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 constexpr long kMaxElems = 0x7fffffffL;
 
+// a * b, saturated at LONG_MAX (size checks multiply untrusted extents)
+long sat_mul(long a, long b) {
+  long r;
+  return __builtin_mul_overflow(a, b, &r) ? LONG_MAX : r;
+}
+
 int check_desc(const tidar_attn_desc* d, tidar::AttnPlan* plan) {
   if (!d) return fail(TIDAR_E_INVALID, "desc is NULL");
   if (d->dtype != TIDAR_DTYPE_F32 && d->dtype != TIDAR_DTYPE_BF16)
@@ -42,16 +49,17 @@ int check_desc(const tidar_attn_desc* d, tidar::AttnPlan* plan) {
     return fail(TIDAR_E_INVALID, "num_q_heads (%d) is not a multiple of num_kv_heads (%d)", d->num_q_heads,
                 d->num_kv_heads);
   if (d->k < 0 || d->num_blocks < 0) return fail(TIDAR_E_INVALID, "k and num_blocks must be >= 0");
-  if (d->num_blocks > d->k + 1)
-    return fail(TIDAR_E_INVALID, "num_blocks (%d) exceeds k + 1 (%d): block j needs drafts d_1..d_j", d->num_blocks,
-                d->k + 1);
+  if ((long)d->num_blocks > (long)d->k + 1)
+    return fail(TIDAR_E_INVALID, "num_blocks (%d) exceeds k + 1 (%ld): block j needs drafts d_1..d_j", d->num_blocks,
+                (long)d->k + 1);
   if (d->num_blocks > 0 && d->block_len < 1) return fail(TIDAR_E_INVALID, "block_len must be >= 1");
   const long R = (long)d->k + (long)d->num_blocks * (d->num_blocks > 0 ? d->block_len : 0);
   if (R < 1) return fail(TIDAR_E_INVALID, "no query rows (k + num_blocks * block_len == 0)");
   if (R > 65536) return fail(TIDAR_E_UNSUPPORTED, "R = %ld query rows exceeds 65536", R);
   if (d->cache_capacity < 1) return fail(TIDAR_E_INVALID, "cache_capacity must be >= 1");
-  if (d->max_cache_len < 0 || d->max_cache_len > d->cache_capacity)
-    return fail(TIDAR_E_CAPACITY, "max_cache_len %d outside 0..cache_capacity (%d)", d->max_cache_len,
+  if (d->max_cache_len < 0) return fail(TIDAR_E_INVALID, "max_cache_len must be >= 0");
+  if (d->max_cache_len > d->cache_capacity)
+    return fail(TIDAR_E_CAPACITY, "max_cache_len %d exceeds cache_capacity (%d)", d->max_cache_len,
                 d->cache_capacity);
   if (!(d->sm_scale > 0.f) || !isfinite(d->sm_scale))
     return fail(TIDAR_E_INVALID, "sm_scale must be positive and finite");
@@ -62,8 +70,8 @@ int check_desc(const tidar_attn_desc* d, tidar::AttnPlan* plan) {
   } else {
     if (D < 4 || D > 256 || D % 4) return fail(TIDAR_E_UNSUPPORTED, "f32 path needs head_dim in 4..256, multiple of 4");
   }
-  const long qe = (long)d->batch * R * d->num_q_heads * D;
-  const long ce = (long)d->batch * d->num_kv_heads * (long)d->cache_capacity * D;
+  const long qe = sat_mul(sat_mul(sat_mul(d->batch, R), d->num_q_heads), D);
+  const long ce = sat_mul(sat_mul(sat_mul(d->batch, d->num_kv_heads), d->cache_capacity), D);
   if (qe > kMaxElems || ce > kMaxElems) return fail(TIDAR_E_UNSUPPORTED, "tensor too large for 32-bit indexing");
   // 64-key tiles of step keys a query tile may see: the whole causal run in
   // append-prefill mode, else the drafts plus one block
@@ -168,9 +176,13 @@ int tidar_kv_commit(int32_t num_layers, int32_t batch, int32_t num_kv_heads, int
     return fail(TIDAR_E_INVALID, "num_layers, batch, num_kv_heads and head_dim must be >= 1");
   if (k < 0 || step_rows < k) return fail(TIDAR_E_INVALID, "need 0 <= k <= step_rows");
   const int eb = dtype == TIDAR_DTYPE_BF16 ? 2 : 4;
-  if ((head_dim * eb) % 16) return fail(TIDAR_E_UNSUPPORTED, "row of head_dim elements must be a multiple of 16 bytes");
+  const long row_bytes = (long)head_dim * eb;
+  if (row_bytes % 16) return fail(TIDAR_E_UNSUPPORTED, "row of head_dim elements must be a multiple of 16 bytes");
+  // a workgroup walks its k rows in 16-byte pieces with 32-bit counters
+  if (sat_mul(k, row_bytes / 16) > kMaxElems) return fail(TIDAR_E_UNSUPPORTED, "k rows of head_dim too large");
   if (cache_capacity < 1) return fail(TIDAR_E_INVALID, "cache_capacity must be >= 1");
-  if (max_cache_len < 0 || (long)max_cache_len + k > cache_capacity)
+  if (max_cache_len < 0) return fail(TIDAR_E_INVALID, "max_cache_len must be >= 0");
+  if ((long)max_cache_len + k > cache_capacity)
     return fail(TIDAR_E_CAPACITY, "max_cache_len (%d) + k (%d) exceeds cache_capacity (%d)", max_cache_len, k,
                 cache_capacity);
   if (!k_step || !v_step || !k_cache || !v_cache || !accept_len || !cache_len_in || !cache_len_out)
@@ -179,7 +191,7 @@ int tidar_kv_commit(int32_t num_layers, int32_t batch, int32_t num_kv_heads, int
   const void* ptrs[] = {k_step, v_step, k_cache, v_cache};
   for (const void* p : ptrs)
     if (!aligned(p, 16)) return fail(TIDAR_E_INVALID, "tensor pointers must be 16-byte aligned");
-  if ((long)num_layers * batch * num_kv_heads > 0x7fffffffL) return fail(TIDAR_E_UNSUPPORTED, "grid too large");
+  if (sat_mul(sat_mul(num_layers, batch), num_kv_heads) > kMaxElems) return fail(TIDAR_E_UNSUPPORTED, "grid too large");
   tidar::CommitParams p{};
   p.L = num_layers;
   p.B = batch;
@@ -276,7 +288,7 @@ size_t tidar_logprob_workspace_bytes(int32_t rows, int32_t vocab) {
 int tidar_token_logprobs(int32_t rows, int32_t vocab, const float* logits, const int32_t* targets, float* logprobs,
                          int32_t* dev_status, void* workspace, size_t workspace_bytes, void* stream) {
   if (rows < 1 || vocab < 1) return fail(TIDAR_E_INVALID, "need rows >= 1 and vocab >= 1");
-  const long nchunks = (vocab + tidar::logprob_chunk() - 1) / tidar::logprob_chunk();
+  const long nchunks = ((long)vocab + tidar::logprob_chunk() - 1) / tidar::logprob_chunk();
   if ((long)rows * vocab > 0x7fffffffL || (long)rows * nchunks > 0x7fffffffL)
     return fail(TIDAR_E_UNSUPPORTED, "logits too large");
   if (!logits || !targets || !logprobs) return fail(TIDAR_E_INVALID, "a required pointer is NULL");

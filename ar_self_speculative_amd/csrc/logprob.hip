@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void lp_final_kernel(LogprobParams p) {
 }  // namespace
 
 size_t logprob_workspace_bytes(int rows, int V) {
-  const size_t nchunks = (size_t)(V + kChunk - 1) / kChunk;
+  const size_t nchunks = ((size_t)V + kChunk - 1) / kChunk;
   return ((size_t)rows * nchunks * sizeof(float2) + 255) / 256 * 256;
 }
 

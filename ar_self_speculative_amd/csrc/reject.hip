@@ -429,7 +429,7 @@ __global__ __launch_bounds__(kThreads) void rej_pick_kernel(RejectParams p) {
 }  // namespace
 
 size_t reject_workspace_bytes(int B, int k, int V) {
-  const size_t nchunks = (size_t)(V + kChunk - 1) / kChunk;
+  const size_t nchunks = ((size_t)V + kChunk - 1) / kChunk;
   size_t bytes = 0;
   bytes += ((size_t)B * (2 * k + 1) * nchunks * sizeof(float2) + 255) / 256 * 256;
   bytes += ((size_t)2 * B * nchunks * sizeof(double) + 255) / 256 * 256;
@@ -440,7 +440,7 @@ size_t reject_workspace_bytes(int B, int k, int V) {
 
 void plan_reject(RejectParams& p) {
   p.chunk = kChunk;
-  p.nchunks = (p.V + kChunk - 1) / kChunk;
+  p.nchunks = (int)(((long)p.V + kChunk - 1) / kChunk);
 }
 
 int reject_max_k() { return kMaxK; }
