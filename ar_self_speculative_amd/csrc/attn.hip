@@ -159,6 +159,9 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 constexpr int kCPS = 2048 + 128;  // bytes per column pair in LDS
 
+// cache-policy operand of the buffer-store builtins: sc1 (device scope)
+constexpr int kStoreDevice = 16;
+
 template <int D>
 struct Lay {
   static constexpr int NCP = D / 16;             // column pairs
@@ -718,16 +721,25 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
         *reinterpret_cast<__attribute__((address_space(3))) bf16x4*>(stage + l32 * PITCH + 2 * d) = v;
       }
     __syncthreads();  // the group's rows are complete in LDS (cheap: once per workgroup)
+    // The stores carry device scope (sc1), which writes them through the
+    // XCD's L2 as they retire. Plain stores would leave the whole output
+    // dirty in L2 (16.5 MB of split partials at the Qwen3-8B step shape),
+    // and the end of the kernel writes every dirty line back before the
+    // merge may start; written through, that traffic drains while other
+    // workgroups still compute. Offsets stay below 2^32: the output holds
+    // fewer than 2^31 elements of 2 bytes (checked on the host).
     u16* const obase = p.S == 1 ? reinterpret_cast<u16*>(p.out)
                                 : reinterpret_cast<u16*>(p.part_o) + (size_t)s * p.B * p.R * p.Hq * D;
+    const __amdgpu_buffer_rsrc_t orsrc = make_rsrc(obase, 0xFFFFFFFFu);
 #pragma unroll
     for (int j = 0; j < PASSES; ++j) {
       const int f = j * 64 + lane;
       const int row = f / CHUNKS, c = f % CHUNKS;
       const uint32_t orow = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(stage + row * PITCH + 2 * D);
       if (orow == 0xFFFFFFFFu) continue;  // past the last query row
-      *reinterpret_cast<u32x4*>(obase + (size_t)orow * D + 8 * c) =
-          *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(stage + row * PITCH + 16 * c);
+      const u32x4 val = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(stage + row * PITCH + 16 * c);
+      __builtin_amdgcn_raw_buffer_store_b128(val, orsrc, (int)(orow * (uint32_t)(2 * D) + 16u * (uint32_t)c), 0,
+                                             kStoreDevice);
     }
   }
 }
@@ -924,7 +936,10 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       w4[i] = (uint32_t)f32_to_bf16_bits(acc[2 * i] * inv) | ((uint32_t)f32_to_bf16_bits(acc[2 * i + 1] * inv) << 16);
-    *reinterpret_cast<uint4*>(reinterpret_cast<u16*>(p.out) + row * D + d) = pk;
+    // written through L2 as in the main kernel's epilogue (byte offsets < 2^32)
+    const u32x4 pv = {pk.x, pk.y, pk.z, pk.w};
+    __builtin_amdgcn_raw_buffer_store_b128(pv, make_rsrc(p.out, 0xFFFFFFFFu), (int)((uint32_t)(row * D + d) * 2u), 0,
+                                           kStoreDevice);
   } else {
     *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + row * D + d) =
         make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[VEC - 1] * inv);
