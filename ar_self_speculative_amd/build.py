@@ -37,9 +37,10 @@ def _hipcc() -> str:
 
 
 # Per-file extra flags. The attention kernels run with the IEEE mode bit
-# clear: v_max_f32 then needs no quieting of its inputs (the scores never
-# hold NaN: out-of-range keys are loaded as zeros and masked to -inf).
-EXTRA_FLAGS = {"attn.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+# clear: v_max_f32 then needs no quieting of its inputs (masked scores are
+# set to -inf by a select, whatever the key rows held). Their leading scalar
+# arguments are preloaded into scalar registers at dispatch.
+EXTRA_FLAGS = {"attn.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans", "-mllvm", "-amdgpu-kernarg-preload-count=11"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -516,8 +516,27 @@ __device__ __forceinline__ void tile_iter(Wave<D, NQT>& st, lds_u8* __restrict__
   wait_copies();
 }
 
+// The first kernel arguments are the fields the prologue needs before its
+// first loads, as plain scalars: this file is built with kernel-argument
+// preloading, so the dispatch places them in scalar registers and the Q, K[0]
+// and cache-length loads go out without first waiting for a load of the
+// argument block (at launch every workgroup waits on memory at once, and that
+// wait is a large part of a workgroup's life). Small fields come packed two
+// to a dword (each below 2^16, checked on the host).
+struct PreArgs {
+  const int32_t* cache_len;
+  const void* q;
+  const void* k_cache;
+  uint32_t qt_s;     // qtiles | S << 16
+  uint32_t hkv_g;    // Hkv | g << 16
+  uint32_t k_bl;     // k | block_len << 16
+  int R, nwg, cap, chunk, max_len;
+};
+
 template <int D, int NQT, int WAVES>
-__global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kernel(AttnParams p) {
+__global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kernel(
+    const int32_t* __restrict__ a_len, const void* __restrict__ a_q, const void* __restrict__ a_kc, uint32_t a_qt_s,
+    uint32_t a_hkv_g, uint32_t a_k_bl, int a_R, int a_nwg, int a_cap, int a_chunk, int a_max_len, AttnParams p) {
   using W = Wave<D, NQT>;
   using L = Lay<D>;
   constexpr int DSTEPS = D / 16, DT = D / 32;
@@ -538,18 +557,37 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
 
-  int w = remap_xcd((int)__builtin_amdgcn_workgroup_id_x(), p.B * p.Hkv * p.qtiles * p.S);
-  const int qt = w % p.qtiles;
-  w /= p.qtiles;
-  const int s = w % p.S;
-  w /= p.S;
-  const int kvh = w % p.Hkv;
-  const int b = w / p.Hkv;
+  const int qtiles = (int)(a_qt_s & 0xffff), S = (int)(a_qt_s >> 16);
+  const int Hkv = (int)(a_hkv_g & 0xffff), g = (int)(a_hkv_g >> 16);
+  const int kdr = (int)(a_k_bl & 0xffff), bl = (int)(a_k_bl >> 16);
+  int w = remap_xcd((int)__builtin_amdgcn_workgroup_id_x(), a_nwg);
+  const int qt = w % qtiles;
+  w /= qtiles;
+  const int s = w % S;
+  w /= S;
+  const int kvh = w % Hkv;
+  const int b = w / Hkv;
 
-  // Q first: its loads do not depend on the cache length, so they are in
-  // flight while the length is fetched. Rows past M load row 0 (in bounds)
-  // and are zeroed, which keeps the eight loads free of branches.
-  const int M = p.R * p.g;
+  // The first prefix tile's K rows do not depend on the cache length: their
+  // copy goes out first, bounded by the host's max_len instead (rows below
+  // max_len lie inside the cache). Rows at or past the length that it brings
+  // in are masked to -inf before any use; V rows past the length are never
+  // loaded (their copies are bounded by the length), so P V sees only zeros
+  // there.
+  const bool last = (s == S - 1);
+  const int kbeg = s * a_chunk;
+  const int nk_hint = __builtin_amdgcn_readfirstlane(max(0, (last ? a_max_len : min(kbeg + a_chunk, a_max_len)) - kbeg));
+  const size_t head_off = (size_t)(b * Hkv + kvh) * a_cap * D + (size_t)kbeg * D;
+  const uint32_t pvo = copy_voff(lane, D * 2);
+  if (nk_hint > 0)
+    copy_tile<D, WAVES>(make_rsrc(reinterpret_cast<const u16*>(a_kc) + head_off, (uint32_t)nk_hint * (D * 2)), pvo, 0,
+                        D * 2, KB[0], wave);
+
+  // Q next: its loads do not depend on the cache length either, so they are
+  // in flight while the length is fetched. Rows past M load row 0 (in
+  // bounds) and are zeroed, which keeps the eight loads free of branches.
+  const int M = a_R * g;
+  const int Hq = Hkv * g;
   W st;
   st.init_addr(lane);
   RowRule rules[NQT];
@@ -557,10 +595,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
   for (int nt = 0; nt < NQT; ++nt) {
     const int m = qt * BM + wave * WROWS + 32 * nt + l32;
     const bool ok = m < M;
-    const int r = ok ? m / p.g : 0;
-    const int h = kvh * p.g + (ok ? m - r * p.g : 0);
-    rules[nt] = row_rule(r, p.k, p.block_len);
-    const u16* qp = reinterpret_cast<const u16*>(p.q) + ((size_t)(b * p.R + r) * p.Hq + h) * D + 8 * half;
+    const int r = ok ? m / g : 0;
+    const int h = kvh * g + (ok ? m - r * g : 0);
+    rules[nt] = row_rule(r, kdr, bl);
+    const u16* qp = reinterpret_cast<const u16*>(a_q) + ((size_t)(b * a_R + r) * Hq + h) * D + 8 * half;
 #pragma unroll
     for (int i = 0; i < DSTEPS; ++i) {
       const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + 16 * i);
@@ -572,14 +610,12 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
     st.l[nt] = 0.f;
   }
 
-  int len = __builtin_amdgcn_readfirstlane(p.cache_len[b]);  // uniform: keeps the tile loop scalar
-  if (len < 0 || len > p.max_len) {
+  int len = __builtin_amdgcn_readfirstlane(a_len[b]);  // uniform: keeps the tile loop scalar
+  if (len < 0 || len > a_max_len) {
     if (tid == 0 && p.dev_status) atomicOr(p.dev_status, 1);
-    len = min(max(len, 0), p.max_len);
+    len = min(max(len, 0), a_max_len);
   }
-  const bool last = (s == p.S - 1);
-  const int kbeg = s * p.chunk;
-  const int kend = last ? len : min(kbeg + p.chunk, len);
+  const int kend = last ? len : min(kbeg + a_chunk, len);
   const int nk = max(0, kend - kbeg);
 
   const float sl2 = p.scale_log2;
@@ -590,23 +626,22 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
   seq.nk = __builtin_amdgcn_readfirstlane(nk);
   seq.np = __builtin_amdgcn_readfirstlane((nk + kBN - 1) / kBN);
   seq.prb = D * 2;
-  seq.pvo = copy_voff(lane, seq.prb);
-  const size_t head_off = (size_t)(b * p.Hkv + kvh) * p.cap * D + (size_t)kbeg * D;
-  seq.pk = reinterpret_cast<const u16*>(p.k_cache) + head_off;
+  seq.pvo = pvo;
+  seq.pk = reinterpret_cast<const u16*>(a_kc) + head_off;
   seq.pv = reinterpret_cast<const u16*>(p.v_cache) + head_off;
   seq.pbytes = (uint32_t)nk * seq.prb;
   seq.nl0 = seq.nl1 = 0;
   seq.c_lo0 = seq.c_hi0 = seq.c_lo1 = seq.c_hi1 = 0;
-  seq.lrb = (uint32_t)p.Hkv * D * 2;
+  seq.lrb = (uint32_t)Hkv * D * 2;
   seq.lvo = copy_voff(lane, seq.lrb);
-  const size_t step_off = ((size_t)b * p.R * p.Hkv + kvh) * D;
+  const size_t step_off = ((size_t)b * a_R * Hkv + kvh) * D;
   seq.lk = reinterpret_cast<const u16*>(p.k_step) + step_off;
   seq.lv = reinterpret_cast<const u16*>(p.v_step) + step_off;
   seq.lbytes0 = seq.lbytes1 = 0;
   if (last) {
     const int m_lo = qt * BM;
     const int m_hi = min(M, m_lo + BM) - 1;
-    const LocalRanges lr = local_ranges(m_lo / p.g, m_hi / p.g, p.k, p.block_len);
+    const LocalRanges lr = local_ranges(m_lo / g, m_hi / g, kdr, bl);
     // uniform by construction; readfirstlane keeps the tile loop scalar
     const int n = __builtin_amdgcn_readfirstlane(lr.n);
     if (n > 0) {
@@ -635,7 +670,12 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
     // arrive while it and the first maxima run (every workgroup starts at
     // once, so this start-up burst is what the first wait pays for).
     const TileSrc t0 = seq.at(0);
-    copy_tile<D, WAVES>(make_rsrc(t0.k, t0.bytes), t0.vo, t0.row0, t0.row_bytes, KB[0], wave);
+    if (nk == 0 || nk_hint == 0) {
+      // tile 0 is not the first prefix tile: replace whatever the early copy
+      // brought (once it has landed) with the right one
+      wait_copies();
+      copy_tile<D, WAVES>(make_rsrc(t0.k, t0.bytes), t0.vo, t0.row0, t0.row_bytes, KB[0], wave);
+    }
     wait_copies();
     __syncthreads();
     copy_tile<D, WAVES>(make_rsrc(t0.v, t0.bytes), t0.vo, t0.row0, t0.row_bytes, VB[0], wave);
@@ -651,6 +691,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
     st.tile_max(sA, sl2);
     wait_copies();
   }
+  if (ntot == 0) wait_copies();  // the early copy lands before KB[0] is reused for staging
   // iterations whose next tile is a full prefix tile run a loop of their own
   const int tmain = __builtin_amdgcn_readfirstlane(max(0, min(nk / kBN, ntot) - 1));
   int t = 0;
@@ -693,19 +734,19 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
     const int m = qt * BM + wave * WROWS + 32 * nt + l32;
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     if (half == 0) {
-      const int r = m / p.g;
-      const uint32_t orow = (uint32_t)((b * p.R + r) * p.Hq + kvh * p.g + (m - r * p.g));
+      const int r = m / g;
+      const uint32_t orow = (uint32_t)((b * a_R + r) * Hq + kvh * g + (m - r * g));
       *reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(stage + l32 * PITCH + 2 * D) =
           m < M ? orow : 0xFFFFFFFFu;
     }
     if (m < M && half == 0) {
-      const int r = m / p.g;
-      const size_t orow = ((size_t)(b * p.R + r) * p.Hq + kvh * p.g + (m - r * p.g));
-      if (p.S == 1) {
+      const int r = m / g;
+      const size_t orow = ((size_t)(b * a_R + r) * Hq + kvh * g + (m - r * g));
+      if (S == 1) {
         if (p.lse) p.lse[orow] = (st.m[nt] + log2f(ltot)) * 0.69314718055994531f;
       } else {
         // log2-domain log-sum-exp of this split's partial
-        p.part_lse[(size_t)s * p.B * p.R * p.Hq + orow] = ltot > 0.f ? st.m[nt] + log2f(ltot) : kNegInf;
+        p.part_lse[(size_t)s * p.B * a_R * Hq + orow] = ltot > 0.f ? st.m[nt] + log2f(ltot) : kNegInf;
       }
     }
 #pragma unroll
@@ -728,8 +769,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
     // merge may start; written through, that traffic drains while other
     // workgroups still compute. Offsets stay below 2^32: the output holds
     // fewer than 2^31 elements of 2 bytes (checked on the host).
-    u16* const obase = p.S == 1 ? reinterpret_cast<u16*>(p.out)
-                                : reinterpret_cast<u16*>(p.part_o) + (size_t)s * p.B * p.R * p.Hq * D;
+    u16* const obase = S == 1 ? reinterpret_cast<u16*>(p.out)
+                              : reinterpret_cast<u16*>(p.part_o) + (size_t)s * p.B * a_R * Hq * D;
     const __amdgpu_buffer_rsrc_t orsrc = make_rsrc(obase, 0xFFFFFFFFu);
 #pragma unroll
     for (int j = 0; j < PASSES; ++j) {
@@ -1036,18 +1077,27 @@ AttnPlan plan_attn(int dtype, int B, int Hq, int Hkv, int D, int R, int max_len,
 }
 
 hipError_t launch_attn_bf16(const AttnParams& p, hipStream_t stream) {
-  const unsigned grid = (unsigned)((size_t)p.B * p.Hkv * p.qtiles * p.S);
+  const size_t grid = (size_t)p.B * p.Hkv * p.qtiles * p.S;
+  if (grid > 0x7fffffff || p.qtiles > 0xffff || p.S > 0xffff || p.Hkv > 0xffff || p.g > 0xffff || p.k > 0xffff ||
+      p.block_len > 0xffff)
+    return hipErrorInvalidValue;
+  const uint32_t qt_s = (uint32_t)p.qtiles | ((uint32_t)p.S << 16);
+  const uint32_t hkv_g = (uint32_t)p.Hkv | ((uint32_t)p.g << 16);
+  const uint32_t k_bl = (uint32_t)p.k | ((uint32_t)p.block_len << 16);
+#define TIDAR_ATTN_ARGS                                                                                       \
+  p.cache_len, p.q, p.k_cache, qt_s, hkv_g, k_bl, p.R, (int)grid, p.cap, p.chunk, p.max_len, p
   // 128 query rows per workgroup: four waves of 32 rows, or two of 64
   if (p.D == 128 && p.nqt == 1)
-    hipLaunchKernelGGL((attn_bf16_kernel<128, 1, 4>), dim3(grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((attn_bf16_kernel<128, 1, 4>), dim3((unsigned)grid), dim3(256), 0, stream, TIDAR_ATTN_ARGS);
   else if (p.D == 128 && p.nqt == 2)
-    hipLaunchKernelGGL((attn_bf16_kernel<128, 2, 2>), dim3(grid), dim3(128), 0, stream, p);
+    hipLaunchKernelGGL((attn_bf16_kernel<128, 2, 2>), dim3((unsigned)grid), dim3(128), 0, stream, TIDAR_ATTN_ARGS);
   else if (p.D == 64 && p.nqt == 1)
-    hipLaunchKernelGGL((attn_bf16_kernel<64, 1, 4>), dim3(grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((attn_bf16_kernel<64, 1, 4>), dim3((unsigned)grid), dim3(256), 0, stream, TIDAR_ATTN_ARGS);
   else if (p.D == 64 && p.nqt == 2)
-    hipLaunchKernelGGL((attn_bf16_kernel<64, 2, 2>), dim3(grid), dim3(128), 0, stream, p);
+    hipLaunchKernelGGL((attn_bf16_kernel<64, 2, 2>), dim3((unsigned)grid), dim3(128), 0, stream, TIDAR_ATTN_ARGS);
   else
     return hipErrorInvalidValue;
+#undef TIDAR_ATTN_ARGS
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.S == 1) return e;
   return launch_merge(p, true, stream);

@@ -120,7 +120,10 @@ size_t tidar_attn_workspace_bytes(const tidar_attn_desc* desc);
  * q        [B, R, Hq, D]    dtype
  * k_step   [B, R, Hkv, D]   dtype   keys of this step's R tokens
  * v_step   [B, R, Hkv, D]   dtype
- * k_cache  [B, Hkv, cap, D] dtype   this layer's cache; rows >= cache_len[b] are never read
+ * k_cache  [B, Hkv, cap, D] dtype   this layer's cache. Rows at or past cache_len[b] never
+ *                                  affect the result: bf16 k_cache rows below max_cache_len
+ *                                  may be loaded (any bit pattern, NaN included, is masked
+ *                                  out); v_cache rows at or past cache_len[b] are never read
  * v_cache  [B, Hkv, cap, D] dtype
  * cache_len[B] int32        committed prefix length per sequence (device)
  * out      [B, R, Hq, D]    dtype   written
