@@ -914,31 +914,35 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p) {
 // One thread per 8 (bf16) or 4 (fp32) output elements of a row.
 // ---------------------------------------------------------------------------
 template <bool BF16>
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
+// Arguments are plain scalars so that they are preloaded into scalar registers
+// at dispatch and the partial loads need not wait for the argument block.
+__global__ __launch_bounds__(256) void attn_merge_kernel(const void* __restrict__ part_o,
+                                                        const float* __restrict__ part_lse, void* __restrict__ out,
+                                                        float* __restrict__ lse, uint32_t rows, uint32_t D,
+                                                        uint32_t S) {
   constexpr int VEC = BF16 ? 8 : 4;
   constexpr int CH = 8;  // splits whose loads are in flight together
-  const int D = p.D;
-  const int tpr = D / VEC;  // threads per row
-  const size_t rows = (size_t)p.B * p.R * p.Hq;
-  const size_t gid = (size_t)__builtin_amdgcn_workgroup_id_x() * 256 + __builtin_amdgcn_workitem_id_x();
-  const size_t row = gid / tpr;
-  const int d = (int)(gid % tpr) * VEC;
+  const uint32_t tpr = D / VEC;  // threads per row
+  // rows * tpr < 2^31 (the output holds fewer than 2^31 elements)
+  const uint32_t gid = __builtin_amdgcn_workgroup_id_x() * 256u + __builtin_amdgcn_workitem_id_x();
+  const uint32_t row = gid / tpr;
+  const uint32_t d = (gid - row * tpr) * VEC;
   if (row >= rows) return;
   // running merge (reference emax, weight sum, weighted sum), CH splits at a time
   float emax = kNegInf, wsum = 0.f;
   float acc[VEC];
 #pragma unroll
   for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
-  for (int s0 = 0; s0 < p.S; s0 += CH) {
+  for (uint32_t s0 = 0; s0 < S; s0 += CH) {
     float e[CH];
     float x[CH][VEC];
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      const bool in = s0 + j < p.S;
+      const bool in = s0 + j < S;
       const size_t prow = (size_t)(in ? s0 + j : s0) * rows + row;
-      e[j] = in ? p.part_lse[prow] : kNegInf;
+      e[j] = in ? part_lse[prow] : kNegInf;
       if (BF16) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(reinterpret_cast<const u16*>(p.part_o) + prow * D + d);
+        const uint4 raw = *reinterpret_cast<const uint4*>(reinterpret_cast<const u16*>(part_o) + prow * D + d);
         const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -946,7 +950,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
           x[j][2 * i + 1] = __uint_as_float(w4[i] & 0xffff0000u);
         }
       } else {
-        const float4 o = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p.part_o) + prow * D + d);
+        const float4 o = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(part_o) + prow * D + d);
         x[j][0] = o.x;
         x[j][1] = o.y;
         x[j][2] = o.z;
@@ -979,22 +983,26 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnParams p) {
       w4[i] = (uint32_t)f32_to_bf16_bits(acc[2 * i] * inv) | ((uint32_t)f32_to_bf16_bits(acc[2 * i + 1] * inv) << 16);
     // written through L2 as in the main kernel's epilogue (byte offsets < 2^32)
     const u32x4 pv = {pk.x, pk.y, pk.z, pk.w};
-    __builtin_amdgcn_raw_buffer_store_b128(pv, make_rsrc(p.out, 0xFFFFFFFFu), (int)((uint32_t)(row * D + d) * 2u), 0,
+    __builtin_amdgcn_raw_buffer_store_b128(pv, make_rsrc(out, 0xFFFFFFFFu), (int)((row * D + d) * 2u), 0,
                                            kStoreDevice);
   } else {
-    *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + row * D + d) =
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + (size_t)row * D + d) =
         make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[VEC - 1] * inv);
   }
-  if (p.lse && d == 0) p.lse[row] = (emax + log2f(wsum)) * 0.69314718055994531f;
+  if (lse && d == 0) lse[row] = (emax + log2f(wsum)) * 0.69314718055994531f;
 }
 
 hipError_t launch_merge(const AttnParams& p, bool bf16, hipStream_t stream) {
-  const size_t threads = (size_t)p.B * p.R * p.Hq * (p.D / (bf16 ? 8 : 4));
+  const size_t rows = (size_t)p.B * p.R * p.Hq;
+  const size_t threads = rows * (p.D / (bf16 ? 8 : 4));
+  if (threads > 0x7fffffff) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)((threads + 255) / 256);
   if (bf16)
-    hipLaunchKernelGGL(attn_merge_kernel<true>, dim3(grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(attn_merge_kernel<true>, dim3(grid), dim3(256), 0, stream, p.part_o, p.part_lse, p.out, p.lse,
+                       (uint32_t)rows, (uint32_t)p.D, (uint32_t)p.S);
   else
-    hipLaunchKernelGGL(attn_merge_kernel<false>, dim3(grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(attn_merge_kernel<false>, dim3(grid), dim3(256), 0, stream, p.part_o, p.part_lse, p.out,
+                       p.lse, (uint32_t)rows, (uint32_t)p.D, (uint32_t)p.S);
   return hipGetLastError();
 }
 
