@@ -54,6 +54,17 @@ __device__ __forceinline__ double wave_sumd(double x) {
   return x;
 }
 
+__device__ __forceinline__ int wave_min_i(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ int wave_max_i(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o));
+  return x;
+}
+
 // Block reductions with a fixed combination order (waves 0..3 in sequence).
 __device__ __forceinline__ float block_max(float x, float* red) {
   x = wave_max(x);
@@ -199,16 +210,26 @@ __device__ __forceinline__ float2 merge_row_wave(const RejectParams& p, int b, i
   return make_float2(m, wave_sumf(z));
 }
 
-// The same merge from statistics staged in LDS.
-__device__ __forceinline__ float2 merge_row_lds(const float2* st, int nchunks, int lane) {
+// Merge the staged per-chunk statistics of every row at once: kGroup lanes
+// per row, lane j of a group taking chunks j, j + kGroup, ... (a fixed order,
+// so the result is deterministic). Returns the row's (max, sum exp) in the
+// group's lane 0 for row `rr` (rr >= nrows: no row).
+constexpr int kGroup = 8;
+__device__ __forceinline__ float2 merge_row_group(const float2* st, int nchunks, int rr, int nrows, int gl) {
   float m = kNegInf;
-  for (int c = lane; c < nchunks; c += 64) m = fmaxf(m, st[c].x);
-  m = wave_max(m);
+  if (rr < nrows)
+    for (int c = gl; c < nchunks; c += kGroup) m = fmaxf(m, st[rr * nchunks + c].x);
+#pragma unroll
+  for (int o = kGroup / 2; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kGroup));
   float z = 0.f;
-  if (m != kNegInf)
-    for (int c = lane; c < nchunks; c += 64)
-      if (st[c].x != kNegInf) z += st[c].y * expf(st[c].x - m);
-  return make_float2(m, wave_sumf(z));
+  if (rr < nrows && m != kNegInf)
+    for (int c = gl; c < nchunks; c += kGroup) {
+      const float2 v = st[rr * nchunks + c];
+      if (v.x != kNegInf) z += v.y * expf(v.x - m);
+    }
+#pragma unroll
+  for (int o = kGroup / 2; o > 0; o >>= 1) z += __shfl_xor(z, o, kGroup);
+  return make_float2(m, z);
 }
 
 // Inclusive prefix sum over the block in thread order (fp64); `tot` gets the
@@ -271,10 +292,15 @@ __global__ __launch_bounds__(kThreads) void rej_resid_kernel(RejectParams p) {
     }
     __syncthreads();
   }
-  for (int rr = wave; rr < nrows; rr += kThreads / 64) {
-    const float2 v = total <= kStage ? merge_row_lds(st_lds + rr * p.nchunks, p.nchunks, lane)
-                                     : merge_row_wave(p, b, rr, lane);
-    if (lane == 0) {
+  // each row merged by a group of kGroup lanes (all rows at once when the
+  // statistics fit in LDS), else by one wave per row from global memory
+  const bool staged = total <= kStage;
+  const int nr_pass = staged ? kThreads / kGroup : kThreads / 64;
+  for (int rr0 = 0; rr0 < nrows; rr0 += nr_pass) {
+    const int rr = rr0 + (staged ? (int)threadIdx.x / kGroup : wave);
+    const float2 v = staged ? merge_row_group(st_lds, p.nchunks, rr, nrows, threadIdx.x % kGroup)
+                            : (rr < nrows ? merge_row_wave(p, b, rr, lane) : make_float2(0.f, 0.f));
+    if (rr < nrows && (staged ? threadIdx.x % kGroup == 0 : lane == 0)) {
       mz[rr] = v;
       if (c == 0) p.row_mz[(size_t)b * nrows + rr] = v;
       if (!(isfinite(v.x) && v.y > 0.f && isfinite(v.y)) && c == 0 && p.dev_status) atomicOr(p.dev_status, 8);
@@ -381,8 +407,13 @@ __global__ __launch_bounds__(kThreads) void rej_pick_kernel(RejectParams p) {
       if (mf == 0x7fffffff && run + sums[c] > target) mf = c;
       run += sums[c];
     }
-    if (mf != 0x7fffffff) atomicMin(&pick_c, mf);
-    if (ml >= 0) atomicMax(&last_c, ml);
+    // one LDS atomic per wave (per-thread atomics on one word serialise)
+    mf = wave_min_i(mf);
+    ml = wave_max_i(ml);
+    if ((threadIdx.x & 63) == 0) {
+      if (mf != 0x7fffffff) atomicMin(&pick_c, mf);
+      if (ml >= 0) atomicMax(&last_c, ml);
+    }
   }
   __syncthreads();
   const int cp = pick_c != 0x7fffffff ? pick_c : max(last_c, 0);
@@ -420,8 +451,12 @@ __global__ __launch_bounds__(kThreads) void rej_pick_kernel(RejectParams p) {
       if (w[j] > 0.f) mine_last = t;
     }
   }
-  if (mine_first != 0x7fffffff) atomicMin(&first_t, mine_first);
-  if (mine_last >= 0) atomicMax(&last_t, mine_last);
+  mine_first = wave_min_i(mine_first);
+  mine_last = wave_max_i(mine_last);
+  if ((threadIdx.x & 63) == 0) {
+    if (mine_first != 0x7fffffff) atomicMin(&first_t, mine_first);
+    if (mine_last >= 0) atomicMax(&last_t, mine_last);
+  }
   __syncthreads();
   if (threadIdx.x == 0) p.next_token[b] = first_t != 0x7fffffff ? first_t : max(last_t, 0);
 }
