@@ -152,6 +152,7 @@ int tidar_attn_step(const tidar_attn_desc* desc, const void* q, const void* k_st
   p.chunk = plan.chunk;
   p.qtiles = plan.qtiles;
   p.nqt = plan.nqt;
+  p.waves = plan.waves;
   p.sm_scale = desc->sm_scale;
   p.scale_log2 = desc->sm_scale * 1.4426950408889634f;
   if (plan.S > 1) {

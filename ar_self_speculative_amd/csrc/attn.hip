@@ -724,12 +724,13 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
   constexpr int PITCH = 2 * D + 16;
   constexpr int CHUNKS = D / 8;                 // 16-byte pieces per row
   constexpr int PASSES = 32 * CHUNKS / 64;      // store instructions per group
-  static_assert(WAVES * NQT == 4 && 32 * PITCH <= L::TILE_BYTES, "staging does not fit");
+  constexpr int GROUPS = WAVES * NQT;  // 32-row groups of the workgroup, GROUPS / 4 per tile buffer
+  static_assert((GROUPS == 4 || GROUPS == 8) && (GROUPS / 4) * 32 * PITCH <= L::TILE_BYTES, "staging does not fit");
   __syncthreads();  // every wave is done with the last tile's K and V
 #pragma unroll
   for (int nt = 0; nt < NQT; ++nt) {
-    const int grp = wave * NQT + nt;
-    lds_u8* const stage = grp == 0 ? KB[0] : grp == 1 ? KB[1] : grp == 2 ? VB[0] : VB[1];
+    const int grp = wave * NQT + nt, gb = grp % 4;
+    lds_u8* const stage = (gb == 0 ? KB[0] : gb == 1 ? KB[1] : gb == 2 ? VB[0] : VB[1]) + (grp / 4) * 32 * PITCH;
     const float ltot = half_sum(st.l[nt]);
     const int m = qt * BM + wave * WROWS + 32 * nt + l32;
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
@@ -1017,8 +1018,10 @@ AttnPlan plan_attn(int dtype, int B, int Hq, int Hkv, int D, int R, int max_len,
   if (dtype == 1) {
     // 32 or 64 query rows per wave; TIDAR_ATTN_WAVE_ROWS overrides the choice (tuning knob)
     pl.nqt = 1;
+    pl.waves = 4;
     if (const char* e = getenv("TIDAR_ATTN_WAVE_ROWS")) pl.nqt = atoi(e) >= 64 ? 2 : 1;
-    pl.bm = kBM;
+    if (const char* e = getenv("TIDAR_ATTN_WAVES")) pl.waves = (atoi(e) == 8 && pl.nqt == 1) ? 8 : 4;
+    pl.bm = pl.waves == 8 ? 2 * kBM : kBM;
     pl.qtiles = (int)((M + pl.bm - 1) / pl.bm);
     base = (long)B * Hkv * pl.qtiles;
   } else {
@@ -1052,8 +1055,10 @@ AttnPlan plan_attn(int dtype, int B, int Hq, int Hkv, int D, int R, int max_len,
       const int se = ntiles > 0 ? (ntiles + ch - 1) / ch : 1;
       if (se != st) continue;  // the same plan as a smaller count
       const long wgs = base * se;
-      const long rounds = (wgs + 511) / 512;
-      const double t = wgs <= 256 ? t1 : t2;
+      // 8-wave workgroups: one per CU, two waves per SIMD already
+      const long slots = pl.waves == 8 ? 256 : 512;
+      const long rounds = (wgs + slots - 1) / slots;
+      const double t = (pl.waves == 8 || wgs > 256) ? t2 : t1;
       const int n_last = ntiles - (se - 1) * ch + local_tiles;
       const double cost = rounds * (F + std::max(ch, n_last) * t) +
                           (se > 1 ? 6000.0 + 2500.0 * ((se + 7) / 8) + se * part_elems * 1.26e-3 : 0.0);
@@ -1095,7 +1100,9 @@ hipError_t launch_attn_bf16(const AttnParams& p, hipStream_t stream) {
 #define TIDAR_ATTN_ARGS                                                                                       \
   p.cache_len, p.q, p.k_cache, qt_s, hkv_g, k_bl, p.R, (int)grid, p.cap, p.chunk, p.max_len, p
   // 128 query rows per workgroup: four waves of 32 rows, or two of 64
-  if (p.D == 128 && p.nqt == 1)
+  if (p.D == 128 && p.nqt == 1 && p.waves == 8)
+    hipLaunchKernelGGL((attn_bf16_kernel<128, 1, 8>), dim3((unsigned)grid), dim3(512), 0, stream, TIDAR_ATTN_ARGS);
+  else if (p.D == 128 && p.nqt == 1)
     hipLaunchKernelGGL((attn_bf16_kernel<128, 1, 4>), dim3((unsigned)grid), dim3(256), 0, stream, TIDAR_ATTN_ARGS);
   else if (p.D == 128 && p.nqt == 2)
     hipLaunchKernelGGL((attn_bf16_kernel<128, 2, 2>), dim3((unsigned)grid), dim3(128), 0, stream, TIDAR_ATTN_ARGS);

@@ -28,6 +28,7 @@ struct AttnParams {
   int chunk;      // prefix keys per split
   int qtiles;     // query tiles per (b, kv head)
   int nqt;        // 32-row query tiles per wave (bf16 path)
+  int waves;      // waves per workgroup (bf16 path)
   float sm_scale;
   float scale_log2;  // sm_scale * log2(e)
 };
@@ -37,6 +38,7 @@ struct AttnPlan {
   int chunk;
   int qtiles;
   int nqt;
+  int waves;
   int bm;          // packed query rows per workgroup
   size_t ws_bytes;
 };

@@ -50,6 +50,23 @@ def test_config2_bf16(seed):
     assert np.abs(lse - rlse).max() <= LSE_TOL["bf16"]
 
 
+@pytest.mark.parametrize("waves", ["8"])
+def test_workgroup_shape_knob_matches_oracle(waves, monkeypatch):
+    """The 8-wave workgroup layout (a tuning knob, TIDAR_ATTN_WAVES) gives the
+    same results within tolerance, including a half-filled last query tile."""
+    monkeypatch.setenv("TIDAR_ATTN_WAVES", waves)
+    c = config_attn(2, seed=5)
+    out, lse = run_attn(c)
+    ref, rlse = _oracle_full(c)
+    assert _report(f"cfg2 bf16 waves={waves}", out, ref, TOL["bf16"]) <= TOL["bf16"]
+    assert np.abs(lse - rlse).max() <= LSE_TOL["bf16"]
+    small = attn_case(dtype="bf16", layers=1, batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, k=4,
+                      num_blocks=5, block_len=4, cache_len=[65, 200], cache_capacity=232, seed=6)
+    out2, _ = run_attn(small)
+    ref2, _ = _oracle_full(small)
+    assert _report(f"small bf16 waves={waves}", out2, ref2, TOL["bf16"]) <= TOL["bf16"]
+
+
 SMALL = [
     # (B, lens, k, num_blocks, block_len, Hq, Hkv, D)
     (1, [0], 4, 5, 4, 4, 1, 128),            # empty prefix: local keys only
