@@ -77,8 +77,16 @@ int check_desc(const tidar_attn_desc* d, tidar::AttnPlan* plan) {
   // append-prefill mode, else the drafts plus one block
   const int local_tiles = d->num_blocks == 0 ? (int)((R + 63) / 64)
                                              : (d->k + 63) / 64 + (d->block_len + 63) / 64;
+  if (d->dtype == TIDAR_DTYPE_BF16 && (d->num_kv_heads > 0xffff || d->num_q_heads / d->num_kv_heads > 0xffff ||
+                                        d->k > 0xffff || (d->num_blocks > 0 && d->block_len > 0xffff)))
+    return fail(TIDAR_E_UNSUPPORTED, "bf16 path: KV heads, group size, k and block_len must be below 65536");
   *plan = tidar::plan_attn(d->dtype, d->batch, d->num_q_heads, d->num_kv_heads, D, (int)R, d->max_cache_len,
                            d->num_splits, local_tiles);
+  // the bf16 kernel receives the tile and split counts packed in 16 bits
+  if (d->dtype == TIDAR_DTYPE_BF16 && (plan->qtiles > 0xffff || plan->S > 0xffff))
+    return fail(TIDAR_E_UNSUPPORTED, "bf16 path: %d query tiles x %d splits exceed 65535", plan->qtiles, plan->S);
+  if ((long)d->batch * d->num_kv_heads * (long)plan->qtiles * plan->S > kMaxElems)
+    return fail(TIDAR_E_UNSUPPORTED, "attention grid too large");
   return TIDAR_OK;
 }
 

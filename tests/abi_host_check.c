@@ -77,6 +77,27 @@ static void check_attn(void) {
       ++failures;
     }
   }
+  {
+    /* bf16 fields the kernel receives packed in 16 bits: refused on the host */
+    tidar_attn_desc w = base_desc();
+    w.num_q_heads = 1 << 17;
+    w.num_kv_heads = 1 << 17;
+    w.k = 0;
+    w.num_blocks = 1;
+    w.block_len = 1;
+    w.cache_capacity = 1;
+    w.max_cache_len = 1;
+    w.head_dim = 64;
+    expect(attn(&w, FAKE, (size_t)1 << 30), TIDAR_E_UNSUPPORTED, "KV heads >= 2^16");
+    tidar_attn_desc sp = base_desc(); /* 2^17 forced splits of a 2^24-key cache */
+    sp.num_q_heads = 1;
+    sp.num_kv_heads = 1;
+    sp.head_dim = 64;
+    sp.cache_capacity = 1 << 24;
+    sp.max_cache_len = 1 << 24;
+    sp.num_splits = 1 << 17;
+    expect(attn(&sp, FAKE, (size_t)1 << 30), TIDAR_E_UNSUPPORTED, "splits >= 2^16");
+  }
   tidar_attn_desc d = base_desc();
   expect(tidar_attn_step(NULL, FAKE, FAKE, FAKE, FAKE, FAKE, (const int32_t*)FAKE, FAKE, NULL, NULL, FAKE,
                          1, NULL),
