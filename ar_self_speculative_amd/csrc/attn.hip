@@ -522,16 +522,8 @@ __device__ __forceinline__ void tile_iter(Wave<D, NQT>& st, lds_u8* __restrict__
 // and cache-length loads go out without first waiting for a load of the
 // argument block (at launch every workgroup waits on memory at once, and that
 // wait is a large part of a workgroup's life). Small fields come packed two
-// to a dword (each below 2^16, checked on the host).
-struct PreArgs {
-  const int32_t* cache_len;
-  const void* q;
-  const void* k_cache;
-  uint32_t qt_s;     // qtiles | S << 16
-  uint32_t hkv_g;    // Hkv | g << 16
-  uint32_t k_bl;     // k | block_len << 16
-  int R, nwg, cap, chunk, max_len;
-};
+// to a dword (each below 2^16, checked on the host): a_qt_s = qtiles | S << 16,
+// a_hkv_g = Hkv | g << 16, a_k_bl = k | block_len << 16; a_nwg is the grid size.
 
 template <int D, int NQT, int WAVES>
 __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kernel(
