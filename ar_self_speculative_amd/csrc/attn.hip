@@ -738,8 +738,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
       if (S == 1) {
         if (p.lse) p.lse[orow] = (st.m[nt] + log2f(ltot)) * 0.69314718055994531f;
       } else {
-        // log2-domain log-sum-exp of this split's partial
-        p.part_lse[(size_t)s * p.B * a_R * Hq + orow] = ltot > 0.f ? st.m[nt] + log2f(ltot) : kNegInf;
+        // log2-domain log-sum-exp of this split's partial, written through like the partial
+        const float e = ltot > 0.f ? st.m[nt] + log2f(ltot) : kNegInf;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(e), make_rsrc(p.part_lse + (size_t)s * p.B * a_R * Hq,
+                                              0xFFFFFFFFu), (int)(orow * 4u), 0, kStoreDevice);
       }
     }
 #pragma unroll
