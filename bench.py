@@ -33,10 +33,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # on a device copy of known size. Valid only for the attention source it was
 # taken on (sha256 prefix of csrc/attn.hip); any other source reports null.
 ATTN_TRAFFIC = {
-    "5ae1add1150d026e": 57072043,
-    # the same kernels: this source differs from the one above in comments only
-    # (identical device assembly apart from the compilation-unit id)
-    "997ab7a7dc7480ae": 57072043,
+    "8ca6ea5ef832f306": 57068743,
 }
 
 SHAPE = dict(layers=36, batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128, P=4096, k=16,
