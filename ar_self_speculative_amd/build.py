@@ -38,9 +38,11 @@ def _hipcc() -> str:
 
 # Per-file extra flags. The attention kernels run with the IEEE mode bit
 # clear: v_max_f32 then needs no quieting of its inputs (masked scores are
-# set to -inf by a select, whatever the key rows held). Their leading scalar
-# arguments are preloaded into scalar registers at dispatch.
-EXTRA_FLAGS = {"attn.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans", "-mllvm", "-amdgpu-kernarg-preload-count=11"]}
+# set to -inf by a select, whatever the key rows held). The attention and
+# sampler kernels' leading scalar arguments are preloaded into scalar
+# registers at dispatch.
+EXTRA_FLAGS = {"attn.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans", "-mllvm", "-amdgpu-kernarg-preload-count=11"],
+               "reject.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=8"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

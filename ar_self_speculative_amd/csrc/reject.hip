@@ -119,26 +119,39 @@ __device__ __forceinline__ void load_chunk(const float* x, int e0, int e1, float
   }
 }
 
-__global__ __launch_bounds__(kThreads) void rej_stats_kernel(RejectParams p) {
+// The three sampler kernels take the fields their first loads need as
+// leading scalar arguments, which the dispatch preloads into scalar registers
+// (this file is built with kernel-argument preloading): the logit, draft and
+// statistics loads then go out without first waiting for the argument block.
+// a_k_nch packs k | nchunks << 16 (k <= 128, nchunks <= 1024).
+__device__ __forceinline__ const float* row_ptr_a(const float* ar, const float* diff, int k, int V, int b, int rr) {
+  return rr <= k ? ar + ((size_t)b * (k + 1) + rr) * V : diff + ((size_t)b * k + (rr - k - 1)) * V;
+}
+
+__global__ __launch_bounds__(kThreads) void rej_stats_kernel(const float* __restrict__ a_ar,
+                                                             const float* __restrict__ a_diff, int a_V,
+                                                             uint32_t a_k_nch, int a_mix, float a_inv_t, float a_lam,
+                                                             float a_mu, RejectParams p) {
   __shared__ float red[4];
-  const int c = blockIdx.x % p.nchunks;
-  const int row = blockIdx.x / p.nchunks;
-  const int nrows = 2 * p.k + 1;
+  const int k = (int)(a_k_nch & 0xffff), nch = (int)(a_k_nch >> 16);
+  const int c = blockIdx.x % nch;
+  const int row = blockIdx.x / nch;
+  const int nrows = 2 * k + 1;
   const int b = row / nrows, rr = row % nrows;
-  const bool target = rr < p.k;  // a verification target (not the bonus row)
-  const float* x = row_ptr(p, b, target && p.mix == 2 ? p.k + 1 + rr : rr);
-  const int e0 = c * kChunk, e1 = min(e0 + kChunk, p.V);
-  const bool vec4 = (p.V & 3) == 0;
+  const bool target = rr < k;  // a verification target (not the bonus row)
+  const float* x = row_ptr_a(a_ar, a_diff, k, a_V, b, target && a_mix == 2 ? k + 1 + rr : rr);
+  const int e0 = c * kChunk, e1 = min(e0 + kChunk, a_V);
+  const bool vec4 = (a_V & 3) == 0;
   float v[kPer];
-  if (target && p.mix == 1) {
+  if (target && a_mix == 1) {
     // mixed target: (lam * a + mu * d) / T, formed exactly as in the draws
     float w[kPer];
     load_chunk(x, e0, e1, 1.f, vec4, v);
-    load_chunk(row_ptr(p, b, p.k + 1 + rr), e0, e1, 1.f, vec4, w);
+    load_chunk(row_ptr_a(a_ar, a_diff, k, a_V, b, k + 1 + rr), e0, e1, 1.f, vec4, w);
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) v[j] = fmaf(p.lam, v[j], p.mu * w[j]) * p.inv_temp;
+    for (int j = 0; j < kPer; ++j) v[j] = fmaf(a_lam, v[j], a_mu * w[j]) * a_inv_t;
   } else {
-    load_chunk(x, e0, e1, p.inv_temp, vec4, v);
+    load_chunk(x, e0, e1, a_inv_t, vec4, v);
   }
   float mx = kNegInf;
 #pragma unroll
@@ -150,7 +163,7 @@ __global__ __launch_bounds__(kThreads) void rej_stats_kernel(RejectParams p) {
     for (int j = 0; j < kPer; ++j) s += expf(v[j] - mx);
   }
   s = block_sumf(s, red);
-  if (threadIdx.x == 0) p.row_stats[((size_t)b * nrows + rr) * p.nchunks + c] = make_float2(mx, s);
+  if (threadIdx.x == 0) p.row_stats[((size_t)b * nrows + rr) * nch + c] = make_float2(mx, s);
 }
 
 // The mixed logit of a verification target (mix == 1), as rej_stats forms it.
@@ -250,15 +263,19 @@ __device__ __forceinline__ double block_scan_incl(double x, double* red, double*
   return x + off;
 }
 
-__global__ __launch_bounds__(kThreads) void rej_resid_kernel(RejectParams p) {
+__global__ __launch_bounds__(kThreads) void rej_resid_kernel(const int32_t* __restrict__ a_drafts,
+                                                             const float* __restrict__ a_uni,
+                                                             const float2* __restrict__ a_stats, uint32_t a_k_nch,
+                                                             RejectParams p) {
   __shared__ float2 mz[2 * kMaxK + 1];
   __shared__ float2 st_lds[kStage];
   __shared__ float rho[kMaxK];
   __shared__ float uni[kMaxK];
   __shared__ int n_sh;
   __shared__ double redd[4];
-  const int c = blockIdx.x % p.nchunks, b = blockIdx.x / p.nchunks;
-  const int k = p.k, nrows = 2 * k + 1;
+  const int k = (int)(a_k_nch & 0xffff), nch = (int)(a_k_nch >> 16);
+  const int c = blockIdx.x % nch, b = blockIdx.x / nch;
+  const int nrows = 2 * k + 1;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   // the draft tokens' logits are gathered first so their latency overlaps
   // the statistics merge
@@ -266,8 +283,8 @@ __global__ __launch_bounds__(kThreads) void rej_resid_kernel(RejectParams p) {
   int d = -1;
   float da = 0.f, dq = 0.f;  // logits of draft i under its target and diffusion rows
   if (i < k) {
-    d = p.drafts[(size_t)b * k + i];
-    uni[i] = p.uniforms[(size_t)b * (k + 1) + i];
+    d = a_drafts[(size_t)b * k + i];
+    uni[i] = a_uni[(size_t)b * (k + 1) + i];
     if (d >= 0 && d < p.V) {
       dq = row_ptr(p, b, k + 1 + i)[d];
       da = p.mix == 2 ? dq : row_ptr(p, b, i)[d];
@@ -276,9 +293,9 @@ __global__ __launch_bounds__(kThreads) void rej_resid_kernel(RejectParams p) {
   }
   // per-row statistics: stage every (row, chunk) pair of this sequence in
   // LDS with one round of loads, then merge each row across one wave
-  const int total = nrows * p.nchunks;
+  const int total = nrows * nch;
   if (total <= kStage) {
-    const float2* g = p.row_stats + (size_t)b * total;
+    const float2* g = a_stats + (size_t)b * total;
     float2 v[kStage / kThreads];
 #pragma unroll
     for (int j = 0; j < kStage / kThreads; ++j) {
@@ -366,27 +383,30 @@ __global__ __launch_bounds__(kThreads) void rej_resid_kernel(RejectParams p) {
   }
 }
 
-__global__ __launch_bounds__(kThreads) void rej_pick_kernel(RejectParams p) {
+__global__ __launch_bounds__(kThreads) void rej_pick_kernel(const int32_t* __restrict__ a_decision,
+                                                            const double* __restrict__ a_sums, uint32_t a_k_nch,
+                                                            int a_B, RejectParams p) {
   __shared__ double red[4];
   __shared__ double sums[kMaxChunks];
   __shared__ int pick_c, last_c, first_t, last_t;
   __shared__ double pick_base;
-  const int b = blockIdx.x, k = p.k, nrows = 2 * k + 1;
-  const int n = p.decision[2 * b];
+  const int k = (int)(a_k_nch & 0xffff), nch = (int)(a_k_nch >> 16);
+  const int b = blockIdx.x, nrows = 2 * k + 1;
+  // thread t owns chunks [cpt*t, cpt*t + cpt)
+  const int cpt = (nch + kThreads - 1) / kThreads;
+  const int c0 = cpt * threadIdx.x, c1 = min(c0 + cpt, nch);
+  double mine = 0.0;
+  for (int c = c0; c < c1; ++c) mine += (sums[c] = a_sums[(size_t)b * nch + c]);
+  const int n = a_decision[2 * b];
   DrawRows dr;
   dr.init(p, b, n, p.row_mz + (size_t)b * nrows);
-  // thread t owns chunks [cpt*t, cpt*t + cpt)
-  const int cpt = (p.nchunks + kThreads - 1) / kThreads;
-  const int c0 = cpt * threadIdx.x, c1 = min(c0 + cpt, p.nchunks);
-  double mine = 0.0;
-  for (int c = c0; c < c1; ++c) mine += (sums[c] = p.resid_sums[(size_t)b * p.nchunks + c]);
   double total;
   double incl = block_scan_incl(mine, red, &total);
   if (!(total > 0.0)) {
     // the residual vanished through rounding: draw from p_n instead
     dr.sub = false;
     mine = 0.0;
-    for (int c = c0; c < c1; ++c) mine += (sums[c] = p.resid_sums[((size_t)p.B + b) * p.nchunks + c]);
+    for (int c = c0; c < c1; ++c) mine += (sums[c] = a_sums[((size_t)a_B + b) * nch + c]);
     incl = block_scan_incl(mine, red, &total);
   }
   const double target = (double)p.uniforms[(size_t)b * (k + 1) + k] * total;
@@ -483,13 +503,16 @@ int reject_max_chunks() { return kMaxChunks; }
 
 hipError_t launch_reject(const RejectParams& p, hipStream_t stream) {
   const unsigned stats_grid = (unsigned)((size_t)p.nchunks * p.B * (2 * p.k + 1));
-  hipLaunchKernelGGL(rej_stats_kernel, dim3(stats_grid), dim3(kThreads), 0, stream, p);
+  const uint32_t k_nch = (uint32_t)p.k | ((uint32_t)p.nchunks << 16);
+  hipLaunchKernelGGL(rej_stats_kernel, dim3(stats_grid), dim3(kThreads), 0, stream, p.ar, p.diff, p.V, k_nch, p.mix,
+                     p.inv_temp, p.lam, p.mu, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(rej_resid_kernel, dim3((unsigned)((size_t)p.nchunks * p.B)), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(rej_resid_kernel, dim3((unsigned)((size_t)p.nchunks * p.B)), dim3(kThreads), 0, stream, p.drafts,
+                     p.uniforms, p.row_stats, k_nch, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(rej_pick_kernel, dim3(p.B), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL(rej_pick_kernel, dim3(p.B), dim3(kThreads), 0, stream, p.decision, p.resid_sums, k_nch, p.B, p);
   return hipGetLastError();
 }
 
