@@ -130,6 +130,23 @@ def test_config3_full_depth_sampled():
     del rng
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_long_draft_block_layout_sampled(dtype):
+    """k = 64: 64 drafts and 65 blocks of 64 masks (R = 4224 rows), so a query
+    tile spans several blocks and the local key ranges of one tile are far
+    apart; sampled rows (every region's first and last rows included)."""
+    c = attn_case(dtype=dtype, layers=1, batch=2, num_q_heads=4, num_kv_heads=1, head_dim=128, k=64,
+                  num_blocks=65, block_len=64, cache_len=[300, 77], cache_capacity=320, seed=21)
+    out, lse = run_attn(c)
+    rows = _sample_rows(c, 40, seed=21)
+    ref, rlse = oracle.attn_rows(*oracle_inputs(c), c.cache_len, rows, k=c.k, num_blocks=c.num_blocks,
+                                 block_len=c.block_len, sm_scale=c.sm_scale)
+    got = np.stack([out[b, r, h] for b, r, h in rows])
+    assert _report(f"k=64 R=4224 {dtype}", got, ref, TOL[dtype]) <= TOL[dtype]
+    got_lse = np.array([lse[b, r, h] for b, r, h in rows])
+    assert np.abs(got_lse - rlse).max() <= LSE_TOL[dtype]
+
+
 @pytest.mark.parametrize("P", [512, 1024, 2048, 4096])
 @pytest.mark.parametrize("R", [1, 8, 16, 32, 64, 128, 256, 512])
 def test_config4_points_sampled(P, R):

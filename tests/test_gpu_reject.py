@@ -93,6 +93,18 @@ def test_ragged_vocab_and_k():
     compare(case0, "k=0 V=4097")
 
 
+def test_max_k_and_statistics_past_the_lds_stage():
+    """k = 128 (the largest the sampler takes) and a vocabulary whose (row, chunk)
+    statistics exceed the LDS stage (257 rows x 25 chunks > 4096), so every row
+    is merged straight from global memory."""
+    case = sampler_case(batch=4, k=128, vocab=100003, ar_sigma=2.0, diff_mode="noisy", diff_sigma=0.3, seed=17)
+    compare(case, "k=128 V=100003 (unstaged statistics)")
+    # identical proposal: every draft accepted, the bonus token drawn from row 128
+    same = sampler_case(batch=2, k=128, vocab=100003, ar_sigma=2.0, diff_mode="noisy", diff_sigma=0.0, seed=18)
+    ref = compare(same, "k=128 V=100003 identical proposal")
+    assert (ref.accept_len == 128).all()
+
+
 def test_temperature():
     case = sampler_case(batch=128, k=3, vocab=1000, ar_sigma=2.0, diff_mode="noisy", diff_sigma=1.0, seed=11,
                         temperature=0.7)
