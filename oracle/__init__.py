@@ -10,9 +10,11 @@ Contents (every function cites the passage it follows):
 
 * ``attention.attn_step``   - hybrid-mask attention by its plain definition,
   per query row over an explicit list of visible keys.
+* ``attention.attn_rows``   - the same definition at chosen (b, r, h)
+  triples (the checker of sampled outputs at full sizes).
 * ``dense.attn_dense``      - independent brute force: a literal 0/1 mask
   matrix built from the region rules, then masked softmax. Used to pin
-  ``attn_step``.
+  ``attn_step`` and ``attn_rows``.
 * ``reject.reject_sample``  - AR rejection sampling of the diffusion drafts
   with residual / bonus resampling by inverse CDF; ``trust_ar`` mixes the
   AR and diffusion logits of the targets (``reject.target_logits``).

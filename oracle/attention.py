@@ -43,6 +43,12 @@ def local_keys(r: int, k: int, num_blocks: int, block_len: int) -> list[int]:
     return list(range(0, j)) + list(range(first, first + block_len))
 
 
+def kv_head(h: int, g: int) -> int:
+    """KV head read by query head h when g query heads share one KV head
+    (contiguous groups)."""
+    return h // g
+
+
 def visible_local_count(k: int, num_blocks: int, block_len: int) -> int:
     """Number of (row, step key) pairs that are visible in one head."""
     R = k + num_blocks * block_len
@@ -78,7 +84,7 @@ def attn_step(q, k_step, v_step, k_cache, v_cache, cache_len, *, k: int,
     for b in range(B):
         n_pre = int(cache_len[b])
         for h in range(Hq):
-            kvh = h // g
+            kvh = kv_head(h, g)
             pre_k = k_cache[b, kvh, :n_pre]
             pre_v = v_cache[b, kvh, :n_pre]
             for r in range(R):
@@ -107,7 +113,7 @@ def attn_rows(q, k_step, v_step, k_cache, v_cache, cache_len, rows, *, k: int,
     out = np.empty((len(rows), D))
     lse = np.empty(len(rows))
     for i, (b, r, h) in enumerate(rows):
-        kvh = h // g
+        kvh = kv_head(h, g)
         n_pre = int(cache_len[b])
         loc = local_keys(r, k, num_blocks, block_len)
         keys = np.concatenate([np.asarray(k_cache[b, kvh, :n_pre], np.float64),

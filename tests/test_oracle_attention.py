@@ -208,3 +208,57 @@ def test_planted_mask_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(oatt, "local_keys", off_by_one)
     bad, _ = _run(c)
     assert np.abs(bad - good).max() > 1e-3
+
+
+def _all_rows(c):
+    return [(b, r, h) for b in range(c.batch) for r in range(c.rows) for h in range(c.num_q_heads)]
+
+
+def _rows_vs_dense(c):
+    """oracle.attn_rows at every (b, r, h) against the dense brute force."""
+    rows = _all_rows(c)
+    o1, l1 = oracle.attn_rows(c.q[0], c.k_step[0], c.v_step[0], c.k_cache[0], c.v_cache[0], c.cache_len, rows,
+                              k=c.k, num_blocks=c.num_blocks, block_len=c.block_len, sm_scale=c.sm_scale)
+    o2, l2 = _run(c, oracle.attn_dense)
+    idx = tuple(np.array(rows).T)
+    return np.abs(o1 - o2[idx]).max(), np.abs(l1 - l2[idx]).max()
+
+
+@settings(max_examples=60, deadline=None)
+@given(B=st.integers(2, 3), k=st.integers(1, 5), blocks=st.sampled_from(["none", "fewer", "all"]),
+       g=st.sampled_from([1, 2, 4]), Hkv=st.integers(1, 2), seed=st.integers(0, 10_000),
+       lens=st.lists(st.integers(0, 24), min_size=3, max_size=3))
+def test_attn_rows_matches_dense_bruteforce(B, k, blocks, g, Hkv, seed, lens):
+    """attn_rows (the sampled-row checker of the full-size parity tests) is
+    pinned to the separately written dense brute force at every (b, r, h):
+    several sequences with ragged prefix lengths (0 included), GQA groups of
+    1, 2 and 4, and no blocks, fewer than k + 1 blocks, or all k + 1."""
+    nb = {"none": 0, "fewer": max(0, k - 1), "all": k + 1}[blocks]
+    cl = np.array(lens[:B], dtype=np.int32)
+    c = _case(int(cl.max()), k, nb, k, g * Hkv, Hkv, B=B, seed=seed, cache_len=cl)
+    e_out, e_lse = _rows_vs_dense(c)
+    assert e_out <= 1e-12 and e_lse <= 1e-12, (e_out, e_lse)
+
+
+def test_attn_rows_planted_head_map_mistake_is_caught(monkeypatch):
+    """A wrong GQA head map (h % Hkv instead of h // g) in attn_rows breaks the pin."""
+    c = _case(9, 3, 4, 3, 4, 2, B=2, seed=4, cache_len=np.array([9, 5], np.int32))
+    assert max(_rows_vs_dense(c)) <= 1e-12
+    monkeypatch.setattr(oatt, "kv_head", lambda h, g: h % 2)
+    assert _rows_vs_dense(c)[0] > 1e-3
+
+
+def test_attn_rows_planted_sequence_length_mistake_is_caught(monkeypatch):
+    """Reading sequence 0's prefix length for every sequence breaks the pin."""
+    c = _case(12, 2, 3, 2, 2, 1, B=2, seed=6, cache_len=np.array([12, 4], np.int32))
+    good = _rows_vs_dense(c)
+    assert max(good) <= 1e-12
+    real = oracle.attn_rows
+
+    def first_len_everywhere(q, ks, vs, kc, vc, cache_len, rows, **kw):
+        return real(q, ks, vs, kc, vc, np.full_like(np.asarray(cache_len), np.asarray(cache_len)[0]), rows, **kw)
+
+    monkeypatch.setattr(oracle, "attn_rows", first_len_everywhere)
+    # the poisoned cache slots past sequence 1's length make the outputs NaN
+    e = _rows_vs_dense(c)[0]
+    assert not (e <= 1e-3), e
