@@ -37,6 +37,9 @@ EXPORTS = (
     "tidar_attn_workspace_bytes", "tidar_attn_step", "tidar_kv_commit",
     "tidar_reject_workspace_bytes", "tidar_reject_sample", "tidar_reject_sample_trust",
     "tidar_logprob_workspace_bytes", "tidar_token_logprobs",
+    # measurement kernels (include/tidar_ceilings.h)
+    "tidar_ceiling_hbm_read", "tidar_ceiling_mfma_bf16", "tidar_ceiling_exp_f32", "tidar_ceiling_fma_f32",
+    "tidar_ceiling_empty",
 )
 
 
@@ -83,6 +86,13 @@ def load() -> ctypes.CDLL:
     lib.tidar_reject_sample_trust.restype = ctypes.c_int
     lib.tidar_reject_sample_trust.argtypes = [i32, i32, i32, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float,
                                               vp, vp, vp, vp, vp, sz, vp]
+    lib.tidar_ceiling_hbm_read.restype = ctypes.c_int
+    lib.tidar_ceiling_hbm_read.argtypes = [vp, sz, ctypes.c_int, vp, vp]
+    for name in ("tidar_ceiling_mfma_bf16", "tidar_ceiling_exp_f32", "tidar_ceiling_fma_f32"):
+        getattr(lib, name).restype = ctypes.c_int
+        getattr(lib, name).argtypes = [ctypes.c_int, ctypes.c_int, vp, vp]
+    lib.tidar_ceiling_empty.restype = ctypes.c_int
+    lib.tidar_ceiling_empty.argtypes = [ctypes.c_int, vp]
     return lib
 
 
@@ -230,3 +240,21 @@ def token_logprobs(*, logits, targets, logprobs, workspace, dev_status=None, str
     _check(_lib.tidar_token_logprobs(rows, V, _ptr(logits), _ptr(targets), _ptr(logprobs), _ptr(dev_status),
                                      _ptr(workspace), workspace.numel() * workspace.element_size(),
                                      _stream(stream)))
+
+
+def ceiling(name: str, *args, stream=None):
+    """Enqueue one measurement kernel of include/tidar_ceilings.h:
+    ceiling("hbm_read", src_tensor, grid, sink), ceiling("mfma_bf16", grid, iters, sink),
+    ceiling("exp_f32" | "fma_f32", grid, iters, sink), ceiling("empty", grid)."""
+    st = _stream(stream)
+    if name == "hbm_read":
+        src, grid, sink = args
+        _dev(src, None, "src")
+        rc = _lib.tidar_ceiling_hbm_read(_ptr(src), src.numel() * src.element_size(), int(grid), _ptr(sink), st)
+    elif name == "empty":
+        rc = _lib.tidar_ceiling_empty(int(args[0]), st)
+    else:
+        grid, iters, sink = args
+        rc = getattr(_lib, "tidar_ceiling_" + name)(int(grid), int(iters), _ptr(sink), st)
+    if rc != 0:
+        raise RuntimeError(f"tidar_ceiling_{name} returned {rc}")

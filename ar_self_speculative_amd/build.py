@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtidar.so")
-SOURCES = ["api.cpp", "attn.hip", "reject.hip", "commit.hip", "logprob.hip"]
+SOURCES = ["api.cpp", "attn.hip", "reject.hip", "commit.hip", "logprob.hip", "ceilings.hip"]
 ARCH = "gfx950"
 
 HIP_FLAGS = [

@@ -1,0 +1,132 @@
+// Measured ceilings of the MI355X (gfx950) for the roofline of the decode
+// step: HBM streaming-read bandwidth, the bf16 MFMA rate, the fp32
+// exponential and FMA issue rates, and the cost of one empty kernel in a
+// stream or graph. These are measurement kernels, not part of the decode
+// step; bench.py times them with events on the stream they are launched on.
+#include "tidar_ceilings.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming read: every thread reads 16-byte pieces with a grid stride, four
+// loads in flight per iteration, and folds them into an xor that is stored
+// only when it equals a value the data cannot produce (the loads stay live).
+__global__ __launch_bounds__(256) void hbm_read_kernel(const u32x4* __restrict__ src, uint64_t n16,
+                                                       uint32_t* __restrict__ sink) {
+  const uint64_t stride = (uint64_t)gridDim.x * 256u;
+  uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4 a = __builtin_nontemporal_load(src + i);
+    const u32x4 b = __builtin_nontemporal_load(src + i + stride);
+    const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
+    const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
+    acc ^= (a ^ b) ^ (c ^ d);
+  }
+  for (; i < n16; i += stride) acc ^= src[i];
+  const uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+  if (x == 0x9e3779b9u) sink[0] = x;
+}
+
+// MFMA issue rate: four independent accumulator chains per wave of
+// v_mfma_f32_32x32x16_bf16 (32768 flops each). Operands come from the lane
+// id so nothing is constant-folded; the sums are stored only under a
+// condition the data cannot meet.
+__global__ __launch_bounds__(256) void mfma_kernel(int iters, float* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(0.001f * (float)(lane + i));
+    b[i] = (__bf16)(0.002f * (float)(lane - i));
+  }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int it = 0; it < iters; ++it) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+  if (s == -1.2345f) sink[0] = s;
+}
+
+// fp32 exponential issue rate: eight independent chains x <- 2^(-x) (the
+// fixed point stays in (0, 1), so no value drifts to inf or denormal).
+__global__ __launch_bounds__(256) void exp_kernel(int iters, float* __restrict__ sink) {
+  float x[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = 0.01f * (float)(threadIdx.x + j);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = __builtin_amdgcn_exp2f(-x[j]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += x[j];
+  if (s == -1.2345f) sink[0] = s;
+}
+
+// fp32 FMA issue rate: eight independent chains x <- x * a + b.
+__global__ __launch_bounds__(256) void fma_kernel(int iters, float a, float b, float* __restrict__ sink) {
+  float x[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = 0.01f * (float)(threadIdx.x + j);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = fmaf(x[j], a, b);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += x[j];
+  if (s == -1.2345f) sink[0] = s;
+}
+
+__global__ void empty_kernel() {}
+
+}  // namespace
+
+extern "C" {
+
+int tidar_ceiling_hbm_read(const void* src, size_t bytes, int grid, uint32_t* sink, void* stream) {
+  if (!src || !sink || grid < 1 || bytes < 16 || (bytes & 15) || (reinterpret_cast<uintptr_t>(src) & 15))
+    return -1;
+  hipLaunchKernelGGL(hbm_read_kernel, dim3((unsigned)grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const u32x4*>(src), (uint64_t)(bytes / 16), sink);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+int tidar_ceiling_mfma_bf16(int grid, int iters, float* sink, void* stream) {
+  if (!sink || grid < 1 || iters < 1) return -1;
+  hipLaunchKernelGGL(mfma_kernel, dim3((unsigned)grid), dim3(256), 0, static_cast<hipStream_t>(stream), iters, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+int tidar_ceiling_exp_f32(int grid, int iters, float* sink, void* stream) {
+  if (!sink || grid < 1 || iters < 1) return -1;
+  hipLaunchKernelGGL(exp_kernel, dim3((unsigned)grid), dim3(256), 0, static_cast<hipStream_t>(stream), iters, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+int tidar_ceiling_fma_f32(int grid, int iters, float* sink, void* stream) {
+  if (!sink || grid < 1 || iters < 1) return -1;
+  hipLaunchKernelGGL(fma_kernel, dim3((unsigned)grid), dim3(256), 0, static_cast<hipStream_t>(stream), iters,
+                     0.999f, 0.001f, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+int tidar_ceiling_empty(int grid, void* stream) {
+  if (grid < 1) return -1;
+  hipLaunchKernelGGL(empty_kernel, dim3((unsigned)grid), dim3(64), 0, static_cast<hipStream_t>(stream));
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+}  // extern "C"

@@ -20,6 +20,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -155,6 +157,182 @@ def _capture(fn):
         fn()
     torch.cuda.synchronize()
     return g
+
+
+def ceilings_bench(args) -> dict:
+    """Measured machine ceilings: HBM streaming read, bf16 MFMA rate, fp32
+    exponential and FMA issue rates, and the cost of an empty kernel launched
+    back to back (from a graph and from the stream). Each kernel is timed with
+    HIP events on the stream it is launched on."""
+    import torch
+
+    import ar_self_speculative_amd as tidar
+
+    dev = torch.device("cuda")
+    sink = torch.zeros(4, dtype=torch.float32, device=dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a, b = ev(), ev()
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e-3  # seconds per call
+
+    out = {}
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    hbm = {}
+    for grid in (1024, 2048, 4096, 8192):
+        t = timed(lambda: tidar.ceiling("hbm_read", buf, grid, sink), 5)
+        hbm[str(grid)] = round(nbytes / t / 1e9, 1)
+    del buf
+    out["hbm_read_gbps_by_grid"] = hbm
+    out["hbm_read_gbps"] = max(hbm.values())
+    out["hbm_read_bytes"] = nbytes
+    grid, iters = 1024, 20000
+    t = timed(lambda: tidar.ceiling("mfma_bf16", grid, iters, sink), 3)
+    flops = grid * 4 * 4 * iters * 32768
+    out["mfma_bf16_tflops"] = round(flops / t / 1e12, 1)
+    # the nominal 2.5 PFLOP/s is 256 CUs x 4 SIMDs x 1024 flops per cycle at 2.4 GHz
+    out["mfma_implied_clock_ghz"] = round(flops / t / (1024 * 1024) / 1e9, 3)
+    grid, iters = 2048, 20000
+    n = grid * 256 * 8 * iters
+    t_exp = timed(lambda: tidar.ceiling("exp_f32", grid, iters, sink), 3)
+    t_fma = timed(lambda: tidar.ceiling("fma_f32", grid, iters, sink), 3)
+    out["exp_f32_gops"] = round(n / t_exp / 1e9, 1)
+    out["fma_f32_gops"] = round(n / t_fma / 1e9, 1)
+    # cycles one SIMD spends per wave64 instruction, at the clock implied by the MFMA run
+    clk = out["mfma_implied_clock_ghz"] * 1e9
+    out["exp_f32_cycles_per_wave_instr"] = round(1024 * clk * 64 / (n / t_exp), 2)
+    out["fma_f32_cycles_per_wave_instr"] = round(1024 * clk * 64 / (n / t_fma), 2)
+    for grid in (1, 512):
+        def many():
+            for _ in range(100):
+                tidar.ceiling("empty", grid)
+        g = _capture(many)
+        out[f"empty_kernel_us_graph_grid{grid}"] = round(_time_graph(g, 5) * 1e3 / 100, 3)
+        out[f"empty_kernel_us_stream_grid{grid}"] = round(timed(many, 3) * 1e6 / 100, 3)
+    return out
+
+
+def config5_bench(args) -> None:
+    """Ragged batch at full depth: 8 sequences with prefixes from U{256..4096},
+    k = 8 (80 query rows), 36 Qwen3-8B-shaped layers, 64 chained steps
+    (attention of every layer -> sampler -> commit, each step attending over
+    the prefixes the earlier steps grew). Every step's inputs are drawn on the
+    device beforehand; the 64 steps are captured in one graph and timed with
+    HIP events on the launch stream. The two cache-length buffers alternate,
+    so no copy sits between steps."""
+    import torch
+
+    import ar_self_speculative_amd as tidar
+    from tidar_synth import CONFIGS, config5_lengths, fill_device_step, fill_verifier_device
+
+    c = CONFIGS[5]
+    L, B, k, cap, n_steps = c["layers"], c["batch"], c["k"], c["cap"], c["steps"]
+    Hq, Hkv, D, V = c["num_q_heads"], c["num_kv_heads"], c["head_dim"], c["vocab"]
+    sigma = c["sampler"]["diff_sigma"]
+    lens0 = config5_lengths(0)
+    W = k * n_steps
+    step = tidar.DecodeStep(layers=L, batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, k=k,
+                            cache_capacity=cap, max_cache_len=int(lens0.max()) + W, vocab=V)
+    R = step.R
+    fill_device_step(step, seed=5, cache_len=lens0)
+    dev = step.q.device
+    g = torch.Generator(device=dev).manual_seed(77)
+    bf = lambda shape: torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    ins = []
+    for _ in range(n_steps):
+        d = dict(q=bf((L, B, R, Hq, D)), ks=bf((L, B, R, Hkv, D)), vs=bf((L, B, R, Hkv, D)),
+                 ar=torch.empty((B, k + 1, V), device=dev), diff=torch.empty((B, k, V), device=dev),
+                 drafts=torch.empty((B, k), dtype=torch.int32, device=dev),
+                 u=torch.empty((B, k + 1), device=dev),
+                 acc=torch.zeros(B, dtype=torch.int32, device=dev),
+                 nxt=torch.zeros(B, dtype=torch.int32, device=dev),
+                 ratio=torch.zeros((B, k), device=dev))
+        fill_verifier_device(d["ar"], d["diff"], d["drafts"], d["u"], g, ar_sigma=3.0, diff_sigma=sigma)
+        ins.append(d)
+    lens = [torch.from_numpy(lens0.copy()).to(dev), torch.empty(B, dtype=torch.int32, device=dev)]
+    status = step.dev_status
+
+    def run_steps():
+        for s_, d in enumerate(ins):
+            lin, lout = lens[s_ % 2], lens[(s_ + 1) % 2]
+            for layer in range(L):
+                tidar.attn_step(step.desc, d["q"][layer], d["ks"][layer], d["vs"][layer], step.k_cache[layer],
+                                step.v_cache[layer], lin, step.out[layer], None, status, step.attn_ws)
+            tidar.reject_sample(ar_logits=d["ar"], diff_logits=d["diff"], drafts=d["drafts"], uniforms=d["u"],
+                                accept_len=d["acc"], next_token=d["nxt"], ratio=d["ratio"], dev_status=status,
+                                workspace=step.rej_ws)
+            tidar.kv_commit(num_layers=L, batch=B, num_kv_heads=Hkv, head_dim=D, k=k, step_rows=R,
+                            cache_capacity=cap, max_cache_len=step.max_len, dtype=tidar.DTYPE_BF16,
+                            k_step=d["ks"], v_step=d["vs"], k_cache=step.k_cache, v_cache=step.v_cache,
+                            accept_len=d["acc"], cache_len_in=lin, cache_len_out=lout, dev_status=status)
+
+    reset = lambda: lens[0].copy_(torch.from_numpy(lens0.copy()).to(dev))
+    run_steps()                                       # eager warm-up pass
+    reset()
+    graph = _capture(run_steps)
+    times = []
+    for _ in range(max(1, args.steps if args.steps < 10 else 3)):
+        reset()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        graph.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        times.append(t0.elapsed_time(t1) * 1e-3)
+    t = sorted(times)[len(times) // 2]
+    if int(status.item()):
+        print(f"device status flags set: {int(status.item())}", file=sys.stderr)
+        sys.exit(1)
+    acc = torch.stack([d["acc"] for d in ins]).cpu().numpy()          # [steps, B]
+    ratio = torch.stack([d["ratio"] for d in ins]).cpu().numpy()
+    uu = torch.stack([d["u"] for d in ins]).cpu().numpy()
+    committed = acc + 1
+    # acceptance tests within 1e-5 of their threshold (by the GPU's own ratios), among those consulted
+    near = 0
+    for s_ in range(n_steps):
+        for b in range(B):
+            n = int(acc[s_, b])
+            tested = np.arange(min(n + 1, k))
+            near += int(np.any(np.abs(uu[s_, b, tested] - np.minimum(1.0, ratio[s_, b, tested])) < 1e-5))
+    # algorithmic bytes and flops, from the lengths each step attended over
+    local = k * (k + 1) // 2 + sum(k * (j + k) for j in range(k + 1))
+    lens_at = lens0[None, :] + np.concatenate([np.zeros((1, B), np.int64), np.cumsum(acc, axis=0)[:-1]])
+    e = 2
+    kv_bytes = float(L * (2 * Hkv * D * e * lens_at.sum() + n_steps * B * 2 * R * Hkv * D * e))
+    qo_bytes = float(L * n_steps * B * 2 * R * Hq * D * e)
+    samp_bytes = float(n_steps * B * (2 * k + 1) * V * 4)
+    commit_bytes = float(2 * 2 * L * acc.sum() * Hkv * D * e)
+    flops = float(L * 4 * Hq * D * (R * lens_at.sum() + n_steps * B * local))
+    all_bytes = kv_bytes + qo_bytes + samp_bytes + commit_bytes
+    t_hbm, t_mfma = all_bytes / (HBM_PEAK_GBPS * 1e9), flops / (BF16_MFMA_PEAK_TFLOPS * 1e12)
+    print(json.dumps({
+        "metric": "ragged-batch TiDAR decode steps/sec (8 sequences, k=8, 36 layers, 64 chained steps)",
+        "value": round(n_steps / t, 2), "unit": "steps/s", "n_gpus": 1, "steps": n_steps, "higher_is_better": True,
+        "ms_per_step": round(t / n_steps * 1e3, 4), "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "qwen3-8b-shape ragged batch: 8 sequences, prefixes U{256..4096}, k=8 (80 query "
+                               "rows), 36 layers, vocab 151936, 64 chained steps",
+                   "batch": B, "layers": L, "k": k, "query_rows": R, "prefix_lengths": lens0.tolist(),
+                   "diff_sigma": sigma},
+        "tokens_per_s": round(float(committed.sum()) / t, 1),
+        "tokens_per_step_mean": round(float(committed.mean()), 3),
+        "tokens_per_step_hist": np.bincount(committed.ravel(), minlength=k + 2)[1:].tolist(),
+        "accept_near_ties": near,
+        "hbm_gbps_algorithmic": round(all_bytes / t / 1e9, 1),
+        "kv_read_gbps": round(kv_bytes / t / 1e9, 1),
+        "mfma_tflops_algorithmic": round(flops / t / 1e12, 1),
+        "roofline": {"bound": "hbm" if t_hbm > t_mfma else "mfma",
+                     "frac": round(max(t_hbm, t_mfma) / t, 4), "t_hbm_s": t_hbm, "t_mfma_s": t_mfma,
+                     "bytes": all_bytes, "flops": flops},
+    }), flush=True)
 
 
 def likelihood_bench(args) -> None:
@@ -362,6 +540,10 @@ def main():
                     help="only time likelihood mode: one causal forward scoring R tokens (P=4096), and exit")
     ap.add_argument("--loop", action="store_true",
                     help="only time the TiDAR step loop with a random-weight Qwen3-8B-shaped decoder, and exit")
+    ap.add_argument("--config5", action="store_true",
+                    help="only time the ragged batch (8 sequences, k=8, 36 layers, 64 chained steps) and exit")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only measure the machine ceilings (HBM read, MFMA, exp/FMA rates, empty kernel) and exit")
     ap.add_argument("--knee", action="store_true",
                     help="only run the append-prefill sweep, report its knee and the draft length it allows")
     args = ap.parse_args()
@@ -375,6 +557,13 @@ def main():
         return
     if args.likelihood:
         likelihood_bench(args)
+        return
+    if args.config5:
+        config5_bench(args)
+        return
+    if args.ceilings:
+        print(json.dumps({"metric": "measured MI355X ceilings", "n_gpus": 1, "data": "synthetic",
+                          **ceilings_bench(args)}), flush=True)
         return
     if args.knee:
         knee_bench(args)

@@ -1,0 +1,47 @@
+/*
+ * tidar_ceilings.h - measurement kernels of libtidar: the machine ceilings
+ * that the decode step's rooflines are stated against (HBM streaming read,
+ * bf16 MFMA rate, fp32 exponential and FMA issue rates, one empty kernel).
+ * They compute nothing of the method; bench.py times them with HIP events on
+ * the stream they are enqueued on.
+ *
+ * Conventions as in tidar.h: device pointers, enqueue only, no allocation,
+ * no synchronisation. Return 0 on success, -1 for a bad argument (nothing is
+ * launched), -5 when the launch fails.
+ */
+#ifndef TIDAR_CEILINGS_H_
+#define TIDAR_CEILINGS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Reads `bytes` (a positive multiple of 16; src 16-byte aligned) once with a
+ * grid of `grid` 256-thread workgroups, 16-byte loads. `sink` is one device
+ * uint32 that is written only with a value the data cannot produce. */
+int tidar_ceiling_hbm_read(const void* src, size_t bytes, int grid, uint32_t* sink, void* stream);
+
+/* `grid` workgroups of 4 waves; each wave issues 4 * iters
+ * v_mfma_f32_32x32x16_bf16 (32768 flops each) on four independent chains:
+ * grid * 4 * 4 * iters * 32768 flops in all. `sink`: one device float. */
+int tidar_ceiling_mfma_bf16(int grid, int iters, float* sink, void* stream);
+
+/* `grid` workgroups of 256 threads; each thread evaluates 8 * iters fp32
+ * base-2 exponentials (v_exp_f32) on eight independent chains. */
+int tidar_ceiling_exp_f32(int grid, int iters, float* sink, void* stream);
+
+/* Same shape with fp32 FMAs (v_fma_f32) instead of exponentials. */
+int tidar_ceiling_fma_f32(int grid, int iters, float* sink, void* stream);
+
+/* An empty kernel of `grid` workgroups of 64 threads (launch and kernel
+ * boundary cost). */
+int tidar_ceiling_empty(int grid, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TIDAR_CEILINGS_H_ */

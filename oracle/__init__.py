@@ -29,14 +29,14 @@ is "parity unpinned".
 """
 from .attention import attn_step, attn_rows, local_keys, visible_local_count
 from .dense import attn_dense, hybrid_mask_matrix
-from .reject import reject_sample, invcdf, softmax_t, SampleResult, selected_block_rows, target_logits
+from .reject import reject_sample, expected_accept_len, invcdf, softmax_t, SampleResult, selected_block_rows, target_logits
 from .commit import kv_commit
 from .likelihood import token_logprobs, sequence_loglik, log_normaliser
 from . import loop
 
 __all__ = [
     "attn_step", "attn_rows", "local_keys", "visible_local_count", "attn_dense",
-    "hybrid_mask_matrix", "reject_sample", "invcdf", "softmax_t",
+    "hybrid_mask_matrix", "reject_sample", "expected_accept_len", "invcdf", "softmax_t",
     "SampleResult", "selected_block_rows", "target_logits", "kv_commit",
     "token_logprobs", "sequence_loglik", "log_normaliser", "loop",
 ]

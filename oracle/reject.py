@@ -154,6 +154,32 @@ def reject_sample(ar_logits, diff_logits, drafts, uniforms, temperature: float =
     return SampleResult(acc, nxt, ratio, amarg, dmarg, rmass)
 
 
+def expected_accept_len(ar_logits, diff_logits, temperature: float = 1.0, trust_ar: float = 1.0) -> np.ndarray:
+    """E[n] per sequence under the speculative-sampling rule, in closed form.
+
+    A draft d ~ q_m is kept with probability min(1, p_m(d)/q_m(d)), so
+    averaged over d the test passes with probability
+    alpha_m = sum_t min(p_m(t), q_m(t)); the tests run in order and stop at
+    the first rejection, so P(n >= i) = prod_{m < i} alpha_m and
+    E[n] = sum_{i=1..k} prod_{m < i} alpha_m (Leviathan et al., 2023).
+    Shapes as in reject_sample; returns float64 [B]. Committed tokens per step
+    (the pages' tokens per forward) are E[n] + 1.
+    """
+    ar_logits = np.asarray(ar_logits)
+    diff_logits = np.asarray(diff_logits)
+    B, kp1, _ = ar_logits.shape
+    k = kp1 - 1
+    out = np.zeros(B)
+    for b in range(B):
+        reach = 1.0
+        for m in range(k):
+            p = softmax_t(target_logits(ar_logits[b, m], diff_logits[b, m], trust_ar), temperature)
+            q = softmax_t(diff_logits[b, m], temperature)
+            reach *= np.minimum(p, q).sum()
+            out[b] += reach
+    return out
+
+
 def selected_block_rows(k: int, n: int) -> tuple[int, int]:
     """Step rows of the pre-drafted block chosen for accept length n.
 

@@ -55,16 +55,23 @@ def oracle_inputs(case, layer=0):
             case.v_cache[layer])
 
 
-NEAR = 1e-5  # near-tie band of the sampler comparison (fraction of the total mass / of the accept probability)
+NEAR = 1e-5  # acceptance near-tie band: |u_i - min(1, rho_i)| below it (the stated tolerance for accept draws)
+
+# Draw band, in probability units (the draw weights normalised so that p sums
+# to one). The GPU forms every weight in fp32 from per-row statistics
+# (maximum, sum of exponentials over 151936 tokens in 4096-token chunks) and
+# scans them in fp64. A weight's relative error is a few 1e-7 (the exponent
+# y*log2(e)/T - m*log2(e) rounded in fp32 at |y*log2(e)| ~ 20, v_exp_f32, the
+# reciprocal of the sum), so a running sum over weights that total at most
+# one (p) or two (p and q of a residual) moves by at most ~1e-6 per
+# distribution. A draw whose target lies closer than this to a CDF boundary
+# may fall on the token across it.
+DRAW_EPS = 2e-6
 
 
-def draw_candidates(ar_logits, diff_logits, b, n, u_last, temperature=1.0, eps=NEAR, trust_ar=1.0):
-    """Tokens whose inverse-CDF interval meets [target - eps*total, target + eps*total].
-
-    For a draw the oracle flags as a near-tie, the GPU's token must be one of
-    these: a different rounding of the running sum can only move the draw
-    across a boundary that lies inside the band.
-    """
+def draw_weights(ar_logits, diff_logits, b, n, temperature=1.0, trust_ar=1.0):
+    """The oracle's (unnormalised) draw weights after accept length n: the
+    residual max(0, p_n - q_n) (p_n when it vanishes), or p_k for the bonus."""
     import oracle
 
     k = ar_logits.shape[1] - 1
@@ -74,36 +81,80 @@ def draw_candidates(ar_logits, diff_logits, b, n, u_last, temperature=1.0, eps=N
         w = np.maximum(0.0, p - oracle.softmax_t(diff_logits[b, n], temperature))
         if w.sum() == 0.0:
             w = p
-    else:
-        w = p
+        return w
+    return p
+
+
+def draw_candidates(w, u_last, eps_abs=DRAW_EPS):
+    """Tokens an inverse-CDF draw with uniform u_last may return under weights
+    w when the running sums carry an absolute error up to eps_abs: the
+    oracle's token, and any token whose interval meets
+    [target - eps_abs, target + eps_abs]."""
+    import oracle
+
+    t_ref, _ = oracle.invcdf(w, float(u_last))
     cs = np.cumsum(w)
-    total = cs[-1]
-    target = float(u_last) * total
+    target = float(u_last) * cs[-1]
     lo = cs - w
-    return np.nonzero((cs > target - eps * total) & (lo < target + eps * total) & (w > 0))[0]
+    near = np.nonzero((cs > target - eps_abs) & (lo < target + eps_abs) & (w > 0))[0]
+    return sorted(set(near.tolist()) | {int(t_ref)})
+
+
+def accept_outcomes(ratio_b, u_b, n_ref, k):
+    """Accept lengths the GPU may return for one sequence: the oracle's n, and
+    for each consulted acceptance test that is a near-tie, the chain with that
+    one test flipped (the later tests as the oracle evaluates them)."""
+    outs = {int(n_ref)}
+    a = np.minimum(1.0, ratio_b)
+    for i in range(min(int(n_ref) + 1, k)):          # tests 0..n consulted (n = the rejecting one)
+        if abs(float(u_b[i]) - a[i]) >= NEAR:
+            continue
+        if i < n_ref:                                 # an acceptance turned into the rejection
+            outs.add(i)
+        else:                                         # the rejection turned into an acceptance
+            n = i + 1
+            while n < k and float(u_b[n]) < a[n]:
+                n += 1
+            outs.add(n)
+    return outs
+
+
+def check_sequence(ref, b, acc_b, nxt_b, ar_logits, diff_logits, uniforms, temperature=1.0, trust_ar=1.0):
+    """One sequence of check_samples. Returns (accept length differs from the
+    oracle's, token differs from the oracle's draw at the GPU's accept length)."""
+    import oracle
+
+    k = ar_logits.shape[1] - 1
+    outs = accept_outcomes(ref.ratio[b], uniforms[b], ref.accept_len[b], k)
+    assert int(acc_b) in outs, (b, int(acc_b), int(ref.accept_len[b]), sorted(outs))
+    n = int(acc_b)
+    if n == ref.accept_len[b] and ref.draw_margin[b] * ref.residual_mass[b] >= DRAW_EPS:
+        assert nxt_b == ref.next_token[b], (b, int(nxt_b), int(ref.next_token[b]))
+        return False, False
+    w = draw_weights(ar_logits, diff_logits, b, n, temperature, trust_ar)
+    cand = draw_candidates(w, uniforms[b, k])
+    assert int(nxt_b) in cand, (b, n, int(nxt_b), cand[:8])
+    return n != ref.accept_len[b], int(nxt_b) != oracle.invcdf(w, float(uniforms[b, k]))[0]
 
 
 def check_samples(ref, acc, nxt, ar_logits, diff_logits, uniforms, temperature=1.0, trust_ar=1.0):
     """Compare GPU (accept_len, next_token) with the oracle's SampleResult.
 
-    Accept lengths must match unless an acceptance test the oracle consulted
-    is a near-tie. With equal accept lengths the token must match, or (for a
-    draw the oracle flags as a near-tie) lie in the band of boundary tokens.
-    Returns (number of accept near-ties excused, number of draw near-ties).
+    The accept length must be the oracle's, or (where a consulted acceptance
+    test is within NEAR of its threshold) the oracle's chain with that one
+    test flipped. The token must be the oracle's inverse-CDF draw for the
+    accept length the GPU returned, or a token whose interval lies within
+    DRAW_EPS of that draw's target (the GPU's rounding of the running sums).
+    Returns (accept lengths that differ from the oracle's, tokens that differ
+    from the oracle's draw at the GPU's accept length).
     """
     B = len(acc)
-    k = ar_logits.shape[1] - 1
-    excused = draw_near = 0
+    acc_diff = draw_diff = 0
     for b in range(B):
-        if ref.accept_margin[b] < NEAR:
-            excused += 1
-            continue
-        assert acc[b] == ref.accept_len[b], (b, int(acc[b]), int(ref.accept_len[b]))
-        if ref.draw_margin[b] < NEAR:
-            draw_near += 1
-            cand = draw_candidates(ar_logits, diff_logits, b, int(acc[b]), uniforms[b, k], temperature,
-                                   trust_ar=trust_ar)
-            assert nxt[b] in cand, (b, int(nxt[b]), cand[:8])
-        else:
-            assert nxt[b] == ref.next_token[b], (b, int(nxt[b]), int(ref.next_token[b]))
-    return excused, draw_near
+        a, d = check_sequence(ref, b, acc[b], nxt[b], ar_logits, diff_logits, uniforms, temperature, trust_ar)
+        acc_diff += int(a)
+        draw_diff += int(d)
+    # a differing token needs a target within DRAW_EPS of a boundary; with
+    # healthy arithmetic that is rare
+    assert draw_diff <= max(2, B // 20), (draw_diff, B)
+    return acc_diff, draw_diff

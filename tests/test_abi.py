@@ -14,8 +14,12 @@ FAKE = 0x10000  # aligned non-null address; every call below fails validation be
 
 
 def _declared():
-    text = open(os.path.join(ROOT, "include", "tidar.h")).read()
-    return sorted(set(re.findall(r"\b(tidar_[a-z_]+)\s*\(", text)))
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for h in sorted(os.listdir(inc)):
+        if h.endswith(".h"):
+            names |= set(re.findall(r"\b(tidar_[a-z0-9_]+)\s*\(", open(os.path.join(inc, h)).read()))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol():

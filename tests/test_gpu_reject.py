@@ -2,10 +2,11 @@
 tidar_reject_sample_trust) against the fp64 oracle.
 
 Accept lengths and tokens must match bit for bit given the same uniforms.
-Exceptions, counted and printed: a sequence whose consulted acceptance test
-is a near-tie (|u - min(1, rho)| < 1e-5) is excused; a draw within 1e-5 of
-the total mass of a CDF boundary must return one of the tokens whose interval
-meets that band.
+Exceptions, counted and printed (tests/gpu_util.py::check_samples): where a
+consulted acceptance test is a near-tie (|u - min(1, rho)| < 1e-5) the
+accept length may be the oracle's chain with that one test flipped; a draw
+whose target lies within 2e-6 (probability units) of a CDF boundary may
+return the token across it.
 """
 import json
 import os
@@ -53,10 +54,10 @@ def compare(case, name, trust_ar=1.0):
     acc, nxt, ratio = gpu_reject(case.ar_logits, case.diff_logits, case.drafts, case.uniforms,
                                  case.temperature, trust_ar=trust_ar)
     mism = (acc != ref.accept_len) | (nxt != ref.next_token)
-    excused, draw_near = check_samples(ref, acc, nxt, case.ar_logits, case.diff_logits, case.uniforms,
-                                       case.temperature, trust_ar=trust_ar)
-    print(f"[parity] {name}: B={case.batch} mismatches={int(mism.sum())} accept near-ties={excused} "
-          f"draw near-ties={draw_near} mean accept={ref.accept_len.mean():.2f}", flush=True)
+    acc_diff, draw_diff = check_samples(ref, acc, nxt, case.ar_logits, case.diff_logits, case.uniforms,
+                                        case.temperature, trust_ar=trust_ar)
+    print(f"[parity] {name}: B={case.batch} mismatches={int(mism.sum())} accept flips (near-tie)={acc_diff} "
+          f"tokens across a boundary (near-tie)={draw_diff} mean accept={ref.accept_len.mean():.2f}", flush=True)
     finite = np.isfinite(ref.ratio)
     np.testing.assert_allclose(ratio[finite], ref.ratio[finite], rtol=2e-5)
     return ref

@@ -184,3 +184,42 @@ def test_selected_block_rows():
     assert oracle.selected_block_rows(16, 0) == (16, 32)
     assert oracle.selected_block_rows(16, 16) == (16 + 256, 16 + 272)
     assert oracle.selected_block_rows(4, 2) == (12, 16)
+
+
+def test_expected_accept_len_closed_form_pins():
+    """expected_accept_len against Monte-Carlo of reject_sample, and its special
+    cases: identical proposal -> k, proposal disjoint from the target -> 0,
+    one draft -> alpha_0 = 1 - total variation distance."""
+    V, k, N = 16, 4, 20000
+    rng = np.random.default_rng(7)
+    ar = rng.normal(0, 1.5, size=(k + 1, V))
+    diff = ar[:k] + rng.normal(0, 1.0, size=(k, V))
+    e = oracle.expected_accept_len(ar[None], diff[None])[0]
+    _, _, _, res = _trials(V, k, N, seed=7)
+    se = res.accept_len.std() / np.sqrt(N)
+    assert abs(res.accept_len.mean() - e) < 5 * se, (res.accept_len.mean(), e)
+    assert oracle.expected_accept_len(ar[None], ar[None, :k])[0] == pytest.approx(k, abs=1e-12)
+    disjoint_ar = np.full((1, 2, 4), -np.inf)
+    disjoint_ar[0, :, :2] = 0.0
+    disjoint_q = np.full((1, 1, 4), -np.inf)
+    disjoint_q[0, 0, 2:] = 0.0
+    assert oracle.expected_accept_len(disjoint_ar, disjoint_q)[0] == 0.0
+    p, q = sp_softmax(ar[0]), sp_softmax(diff[0])
+    one = oracle.expected_accept_len(ar[None, :2], diff[None, :1])[0]
+    assert one == pytest.approx(1.0 - 0.5 * np.abs(p - q).sum(), abs=1e-12)
+
+
+def test_config5_noise_scale_gives_seven_committed_tokens():
+    """The ragged batch's stored noise scale (written by oracle/calibrate_config5.py)
+    gives a mean of 7 committed tokens per step by the oracle's closed form, over
+    the exact verifier inputs of its 64 steps."""
+    import json
+    import os
+
+    from oracle.calibrate_config5 import mean_committed, step_draws
+    from tidar_synth import CONFIGS
+
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "config5_sigma.json")))
+    assert CONFIGS[5]["sampler"]["diff_sigma"] == g["sigma"]
+    m = mean_committed(step_draws(), g["sigma"])
+    assert abs(m - 7.0) < 0.02, m

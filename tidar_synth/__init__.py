@@ -169,6 +169,28 @@ def draft_from_logits(diff_logits: np.ndarray, rng: np.random.Generator,
     return np.argmax(diff_logits.astype(np.float64) / temperature + g, axis=-1).astype(np.int32)
 
 
+def sampler_draws(*, batch: int, k: int, vocab: int, ar_sigma: float, seed: int = 0):
+    """The first two draws of the verifier recipe from ``seed``: AR logits
+    ~ N(0, ar_sigma) [B, k+1, V] and unit-normal noise [B, k, V] (float32),
+    plus the generator positioned for the draws that follow."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ar = rng.standard_normal((batch, k + 1, vocab), dtype=np.float32) * np.float32(ar_sigma)
+    z = rng.standard_normal((batch, k, vocab), dtype=np.float32)
+    return ar, z, rng
+
+
+def diffusion_logits(ar: np.ndarray, z: np.ndarray, diff_mode: str, diff_sigma: float) -> np.ndarray:
+    """Diffusion logits from the recipe's noise: ``"independent"``: z * sigma;
+    ``"noisy"``: AR logits of rows 0..k-1 + z * sigma (float32)."""
+    k = z.shape[1]
+    noise = z * np.float32(diff_sigma)
+    if diff_mode == "independent":
+        return np.ascontiguousarray(noise)
+    if diff_mode == "noisy":
+        return np.ascontiguousarray((ar[:, :k, :] + noise).astype(np.float32))
+    raise ValueError(diff_mode)
+
+
 def sampler_case(*, batch: int, k: int, vocab: int, ar_sigma: float,
                  diff_mode: str, diff_sigma: float, seed: int = 0,
                  temperature: float = 1.0) -> SamplerCase:
@@ -179,19 +201,12 @@ def sampler_case(*, batch: int, k: int, vocab: int, ar_sigma: float,
     AR logits of rows 0..k-1 + N(0, diff_sigma) noise. Generation order: AR
     logits, diffusion logits/noise, draft-sampling draws, verify uniforms.
     """
-    rng = np.random.Generator(np.random.PCG64(seed))
-    ar = rng.standard_normal((batch, k + 1, vocab), dtype=np.float32) * np.float32(ar_sigma)
-    noise = rng.standard_normal((batch, k, vocab), dtype=np.float32) * np.float32(diff_sigma)
-    if diff_mode == "independent":
-        diff = noise
-    elif diff_mode == "noisy":
-        diff = (ar[:, :k, :] + noise).astype(np.float32)
-    else:
-        raise ValueError(diff_mode)
+    ar, z, rng = sampler_draws(batch=batch, k=k, vocab=vocab, ar_sigma=ar_sigma, seed=seed)
+    diff = diffusion_logits(ar, z, diff_mode, diff_sigma)
     drafts = draft_from_logits(diff, rng, temperature) if k > 0 else np.zeros((batch, 0), np.int32)
     uniforms = rng.random((batch, k + 1), dtype=np.float32)
     return SamplerCase(batch=batch, k=k, vocab=vocab, ar_logits=ar,
-                       diff_logits=np.ascontiguousarray(diff), drafts=drafts,
+                       diff_logits=diff, drafts=drafts,
                        uniforms=uniforms, temperature=temperature)
 
 
@@ -219,8 +234,30 @@ CONFIGS = {
             R=(1, 8, 16, 32, 64, 128, 256, 512)),
     5: dict(name="qwen3-8b-ragged-b8-bf16", dtype="bf16", layers=36, batch=8, num_q_heads=32,
             num_kv_heads=8, head_dim=128, P_range=(256, 4096), k=8, cap=4608,
-            vocab=151936, steps=64),
+            vocab=151936, steps=64,
+            # diffusion noise scale for a mean of ~7 committed tokens per step, found by
+            # bisection on the oracle's closed-form acceptance (tests/golden/config5_sigma.json)
+            sampler=dict(ar_sigma=3.0, diff_mode="noisy", diff_sigma=0.162)),
 }
+
+# verifier inputs of step `it` of the ragged batch come from seed CONFIG5_STEP_SEED0 + it
+CONFIG5_STEP_SEED0 = 50
+
+
+def config5_lengths(seed: int = 0) -> np.ndarray:
+    """Prefix lengths of the ragged batch, U{256..4096} per sequence."""
+    c = CONFIGS[5]
+    rng = np.random.Generator(np.random.PCG64(seed + 104729))
+    return rng.integers(c["P_range"][0], c["P_range"][1] + 1, size=c["batch"]).astype(np.int32)
+
+
+def config5_step_sampler(it: int, *, diff_sigma: float | None = None) -> SamplerCase:
+    """Verifier inputs of step ``it`` of the ragged-batch workload."""
+    c = CONFIGS[5]
+    s = dict(c["sampler"])
+    if diff_sigma is not None:
+        s["diff_sigma"] = diff_sigma
+    return sampler_case(batch=c["batch"], k=c["k"], vocab=c["vocab"], seed=CONFIG5_STEP_SEED0 + it, **s)
 
 
 def config_attn(n: int, *, seed: int = 0, layers: int | None = None, P: int | None = None,
@@ -244,8 +281,7 @@ def config_attn(n: int, *, seed: int = 0, layers: int | None = None, P: int | No
                          num_blocks=0, block_len=1, cache_len=P, cache_capacity=P + R,
                          seed=seed, poison=poison)
     if n == 5:
-        rng = np.random.Generator(np.random.PCG64(seed + 104729))
-        lens = rng.integers(c["P_range"][0], c["P_range"][1] + 1, size=c["batch"]).astype(np.int32)
+        lens = config5_lengths(seed)
         k = c["k"]
         return attn_case(dtype="bf16", layers=L, batch=c["batch"], num_q_heads=c["num_q_heads"],
                          num_kv_heads=c["num_kv_heads"], head_dim=c["head_dim"], k=k,
@@ -262,6 +298,27 @@ def config_sampler(n: int, *, seed: int = 0, diff_sigma: float | None = None,
         s["diff_sigma"] = diff_sigma
     return sampler_case(batch=c["batch"] if batch is None else batch, k=c["k"],
                         vocab=c["vocab"], seed=seed + 1, **s)
+
+
+def fill_verifier_device(ar_logits, diff_logits, drafts, uniforms, g, *, ar_sigma: float = 3.0,
+                         diff_sigma: float = 1.0, temperature: float = 1.0) -> None:
+    """Verifier inputs on the device from torch generator ``g``, same recipe
+    as sampler_case: AR logits ~ N(0, ar_sigma), diffusion logits = AR of
+    rows 0..k-1 + N(0, diff_sigma), drafts by Gumbel-max from the diffusion
+    logits, uniforms in [0, 1). Buffers: [B, k+1, V], [B, k, V], [B, k], [B, k+1]."""
+    import torch
+
+    dev = ar_logits.device
+    ar_logits.normal_(generator=g).mul_(ar_sigma)
+    k = diff_logits.shape[1]
+    if k:
+        noise = torch.randn(diff_logits.shape, generator=g, device=dev) * diff_sigma
+        diff_logits.copy_(ar_logits[:, :k] + noise)
+        u = torch.rand(diff_logits.shape, generator=g, device=dev).clamp_min(1e-30)
+        gumbel = -torch.log(-torch.log(u))
+        drafts.copy_(torch.argmax(diff_logits / temperature + gumbel, dim=-1).to(torch.int32))
+        del noise, u, gumbel
+    uniforms.copy_(torch.rand(uniforms.shape, generator=g, device=dev))
 
 
 def fill_device_step(step, *, seed: int, cache_len, ar_sigma: float = 3.0,
@@ -298,16 +355,8 @@ def fill_device_step(step, *, seed: int, cache_len, ar_sigma: float = 3.0,
     mask = invalid[None, :, None, :, None]
     step.k_cache.masked_fill_(mask, float("nan"))
     step.v_cache.masked_fill_(mask, float("nan"))
-    step.ar_logits.normal_(generator=g).mul_(ar_sigma)
-    k = step.k
-    if k:
-        noise = torch.randn(step.diff_logits.shape, generator=g, device=dev) * diff_sigma
-        step.diff_logits.copy_(step.ar_logits[:, :k] + noise)
-        u = torch.rand(step.diff_logits.shape, generator=g, device=dev).clamp_min(1e-30)
-        gumbel = -torch.log(-torch.log(u))
-        step.drafts.copy_(torch.argmax(step.diff_logits / temperature + gumbel, dim=-1).to(torch.int32))
-        del noise, u, gumbel
-    step.uniforms.copy_(torch.rand(step.uniforms.shape, generator=g, device=dev))
+    fill_verifier_device(step.ar_logits, step.diff_logits, step.drafts, step.uniforms, g,
+                         ar_sigma=ar_sigma, diff_sigma=diff_sigma, temperature=temperature)
     step.accept_len.zero_()
     step.next_token.zero_()
     step.dev_status.zero_()
