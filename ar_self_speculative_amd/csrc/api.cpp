@@ -161,14 +161,19 @@ int tidar_attn_step(const tidar_attn_desc* desc, const void* q, const void* k_st
   p.qtiles = plan.qtiles;
   p.nqt = plan.nqt;
   p.waves = plan.waves;
+  p.decode = plan.decode;
+  p.fused_merge = plan.fused_merge;
   p.sm_scale = desc->sm_scale;
   p.scale_log2 = desc->sm_scale * 1.4426950408889634f;
-  if (plan.S > 1) {
+  if (plan.S > 1 || plan.decode) {
+    // [arrival counters (decode path)] [split outputs] [split log-sum-exps]
     const size_t rows = (size_t)plan.S * p.B * p.R * p.Hq;
     const size_t elem = desc->dtype == TIDAR_DTYPE_BF16 ? 2 : 4;
-    p.part_o = workspace;
+    char* ws = static_cast<char*>(workspace);
+    p.counters = reinterpret_cast<int32_t*>(ws);
+    p.part_o = ws + plan.counter_bytes;
     const size_t o_bytes = (rows * p.D * elem + 255) / 256 * 256;
-    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+    p.part_lse = reinterpret_cast<float*>(ws + plan.counter_bytes + o_bytes);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = desc->dtype == TIDAR_DTYPE_BF16 ? tidar::launch_attn_bf16(p, s) : tidar::launch_attn_f32(p, s);

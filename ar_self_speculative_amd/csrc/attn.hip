@@ -197,6 +197,17 @@ __device__ __forceinline__ uint32_t copy_voff(int lane, uint32_t row_bytes) {
 // wait for this wave's outstanding global->LDS copies
 __device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); /* vmcnt(0) */ }
 
+// Workgroup barrier that orders LDS accesses only: unlike __syncthreads()
+// it does not wait for this wave's global loads (a workgroup-scope release
+// for all address spaces waits on vmcnt(0)). Global-to-LDS copies are
+// vector-memory operations: each wave waits for its own with an explicit
+// vmcnt before the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Per-wave state: NQT tiles of 32 query rows, online softmax in the log2
 // domain. The running maximum is only raised when a tile exceeds it by more
 // than kSlack (probabilities then stay below 2^kSlack), which skips the
@@ -781,6 +792,336 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
 }
 
 // ---------------------------------------------------------------------------
+// Decode-regime kernel: few packed query rows per KV head (M = R * g <= 128,
+// R <= 128), where the step is bound by streaming the prefix K/V from HBM and
+// by latency, not by the matrix work. A workgroup owns one (sequence, KV
+// head) and one split: 128 prefix keys (two 64-key tiles), or, for the last
+// split, the step's own R keys under the region rule. It issues the copies
+// of all its K and V tiles into LDS at entry and then:
+//   phase 1: S^T = K Q^T per (32-row tile, 64-key tile) unit, spread over the
+//            four waves; row maxima are exchanged through LDS, and the
+//            probabilities (rounded to bf16, the row sums from the rounded
+//            values as in the main kernel) are written to LDS in the
+//            B-operand layout of the P V product, over the K tiles;
+//   phase 2: O^T = V^T P^T per (32-row tile, 32-dim tile) unit.
+// Each split stores its normalised output (bf16) and log2-domain LSE like
+// the main kernel's splits. When the partials of a (sequence, KV head) are
+// small, the split that arrives last merges them (arrival counter in the
+// workspace, acquire-release at device scope, reset to zero by the merger);
+// otherwise the merge kernel runs after this one.
+// ---------------------------------------------------------------------------
+constexpr int kDecChunk = 128;   // prefix keys per split
+constexpr int kDecMaxRows = 128; // packed query rows per (sequence, KV head)
+constexpr int kDecMergeLoads = 34;  // partials one thread of the in-kernel merge loads at once
+
+// The body of the decode kernel. The two LDS buffers arrive as restrict
+// pointers: the compiler then knows that the V copies in flight do not write
+// what phase 1 reads, and phase 1 waits for the K copies only.
+template <int D>
+__device__ __forceinline__ void attn_dec_body(lds_u8* __restrict__ kb, lds_u8* __restrict__ vb,
+                                              float (*__restrict__ rmax)[2][32], float (*__restrict__ rsum)[2][32],
+                                              int* __restrict__ last_sh, const int32_t* a_len, const void* a_q,
+                                              const void* a_kc, const void* a_vc, int a_R, int a_cap, int a_max_len,
+                                              int b, int kvh, int s, int NS, int Hkv, int g, int kdr, int bl,
+                                              const AttnParams& p) {
+  using W = Wave<D, 1>;
+  using L = Lay<D>;
+  constexpr int DSTEPS = D / 16, DT = D / 32;
+  const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, half = lane >> 5;
+  const bool local = (s == NS - 1);
+  const int M = a_R * g, Hq = Hkv * g;
+  const int RT = (M + 31) / 32;
+
+  // The keys of this split: [kbeg, kbeg + nk) of the prefix, or the R step
+  // keys. The K copies go out before the cache length arrives, bounded by the
+  // host's max_len (rows past the length that they bring in are masked before
+  // any use); the V copies wait for the length, since rows past it may hold
+  // anything (NaN included) and P V must never read them.
+  const uint32_t prb = D * 2, lrb = (uint32_t)Hkv * D * 2;
+  const int kbeg = s * kDecChunk;
+  const uint16_t* kbase;
+  const uint16_t* vbase;
+  uint32_t rb;
+  if (local) {
+    const size_t off = ((size_t)b * a_R * Hkv + kvh) * D;
+    kbase = reinterpret_cast<const u16*>(p.k_step) + off;
+    vbase = reinterpret_cast<const u16*>(p.v_step) + off;
+    rb = lrb;
+  } else {
+    const size_t off = ((size_t)(b * Hkv + kvh) * a_cap + kbeg) * D;
+    kbase = reinterpret_cast<const u16*>(a_kc) + off;
+    vbase = reinterpret_cast<const u16*>(a_vc) + off;
+    rb = prb;
+  }
+  const uint32_t vo = copy_voff(lane, rb);
+  const int nk_hint = __builtin_amdgcn_readfirstlane(local ? a_R : max(0, min(kDecChunk, a_max_len - kbeg)));
+  const auto bytes_of = [&](int n) { return local ? (uint32_t)(n - 1) * lrb + D * 2 : (uint32_t)n * prb; };
+  // Both K tiles and both V tiles are always copied: copies past the
+  // resource's end return zeros without touching memory.
+  {
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, nk_hint > 0 ? bytes_of(nk_hint) : 0u);
+    copy_tile<D, 4>(rk, vo, 0, rb, kb, wave);
+    copy_tile<D, 4>(rk, vo, kBN, rb, kb + L::TILE_BYTES, wave);
+  }
+
+  // phase 1 units of this wave: u = wave and wave + 4, (row tile, key tile) = (u / 2, u % 2)
+  W st[2];
+  RowRule rules[2][1];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rt = (wave + 4 * i) >> 1;
+    st[i].init_addr(lane);
+    st[i].l[0] = 0.f;
+    const int m = rt * 32 + l32;
+    const bool ok = m < M;
+    const int r = ok ? m / g : 0;
+    const int h = kvh * g + (ok ? m - r * g : 0);
+    rules[i][0] = row_rule(r, kdr, bl);
+    // rows past M (and units with no rows) load row 0, which is in bounds, and
+    // are zeroed: the loads carry no branch, so they all fly together
+    const u16* qp = reinterpret_cast<const u16*>(a_q) + ((size_t)(b * a_R + r) * Hq + h) * D + 8 * half;
+#pragma unroll
+    for (int d = 0; d < DSTEPS; ++d) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + 16 * d);
+      st[i].qf[0][d] = ok ? v : bf16x8{};
+    }
+  }
+
+  int len = __builtin_amdgcn_readfirstlane(a_len[b]);
+  if (len < 0 || len > a_max_len) {
+    if (tid == 0 && p.dev_status) atomicOr(p.dev_status, 1);
+    len = min(max(len, 0), a_max_len);
+  }
+  const int nk = __builtin_amdgcn_readfirstlane(local ? a_R : max(0, min(kDecChunk, len - kbeg)));
+  const int ntiles = (nk + kBN - 1) / kBN;
+  {
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, nk > 0 ? bytes_of(nk) : 0u);
+    copy_tile<D, 4>(rv, vo, 0, rb, vb, wave);
+    copy_tile<D, 4>(rv, vo, kBN, rb, vb + L::TILE_BYTES, wave);
+  }
+  bool has[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int u = wave + 4 * i;
+    has[i] = (u >> 1) < RT && (u & 1) < ntiles;
+  }
+  const float sl2 = p.scale_log2;
+  wait_copies();  // this wave's K and V copies and Q rows have landed
+  lds_barrier();  // every K and V tile is in LDS
+
+  typename W::S sc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int u = wave + 4 * i, rt = u >> 1, kt = u & 1;
+    if (rt >= RT) continue;
+    float t = kNegInf;
+    if (has[i]) {
+      st[i].qk(kb + kt * L::TILE_BYTES, sc[i]);
+      const int nv = min(kBN, nk - kt * kBN);
+      if (local)
+        W::template mask<true>(sc[i], lane, nv, kt * kBN, rules[i]);
+      else if (nv < kBN)
+        W::template mask<false>(sc[i], lane, nv, 0, rules[i]);
+      float mx = kNegInf;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) W::max8(sc[i], 0, q, mx);
+      t = half_max(mx) * sl2;
+    }
+    if (half == 0) rmax[rt][kt][l32] = t;
+  }
+  lds_barrier();  // row maxima published; every read of the K tiles is done
+
+  // P over the K tiles: slot (row tile, key tile, k-step) of 1 KB, one 16-byte B fragment per lane
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int u = wave + 4 * i, rt = u >> 1, kt = u & 1;
+    if (!has[i]) continue;
+    const float mrow = fmaxf(rmax[rt][0][l32], rmax[rt][1][l32]);
+    const float muse = mrow == kNegInf ? 0.f : mrow;
+    typename W::P pb;
+    st[i].probs(sc[i], 0, 0, 32, muse, sl2, pb);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(kb + ((rt * 2 + kt) * 4 + ks) * 1024 +
+                                                                  lane * 16) = pb[0][ks];
+    const float lsum = half_sum(st[i].l[0]);
+    if (half == 0) rsum[rt][kt][l32] = lsum;
+  }
+  lds_barrier();  // P and the row sums are in LDS
+
+  // phase 2: units (row tile, dim tile), u = wave + 4 j
+  W vw;
+  vw.init_addr(lane);
+  u16* const obase = reinterpret_cast<u16*>(p.part_o) + (size_t)s * p.B * a_R * Hq * D;
+  const __amdgpu_buffer_rsrc_t orsrc = make_rsrc(obase, 0xFFFFFFFFu);
+  const __amdgpu_buffer_rsrc_t lrsrc = make_rsrc(p.part_lse + (size_t)s * p.B * a_R * Hq, 0xFFFFFFFFu);
+  for (int u = wave; u < RT * DT; u += 4) {
+    const int rt = u / DT, dt = u % DT;
+    f32x16 o = {};
+    for (int kt = 0; kt < ntiles; ++kt) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 pf = *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+            kb + ((rt * 2 + kt) * 4 + ks) * 1024 + lane * 16);
+        o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vw.vfrag(vb + kt * L::TILE_BYTES, ks, dt), pf, o,
+                                                    0, 0, 0);
+      }
+    }
+    const int m = rt * 32 + l32;
+    if (m >= M) continue;
+    const float ltot = (ntiles > 0 ? rsum[rt][0][l32] : 0.f) + (ntiles > 1 ? rsum[rt][1][l32] : 0.f);
+    const float mrow = fmaxf(rmax[rt][0][l32], rmax[rt][1][l32]);
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    const int r = m / g;
+    const uint32_t orow = (uint32_t)((b * a_R + r) * Hq + kvh * g + (m - r * g));
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d = 32 * dt + 8 * i4 + 4 * half;
+      const uint32_t lo = (uint32_t)f32_to_bf16_bits(o[4 * i4 + 0] * inv) |
+                          ((uint32_t)f32_to_bf16_bits(o[4 * i4 + 1] * inv) << 16);
+      const uint32_t hi = (uint32_t)f32_to_bf16_bits(o[4 * i4 + 2] * inv) |
+                          ((uint32_t)f32_to_bf16_bits(o[4 * i4 + 3] * inv) << 16);
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, orsrc, (int)(orow * (uint32_t)(2 * D) + 2u * (uint32_t)d), 0,
+                                            kStoreDevice);
+    }
+    if (dt == 0 && half == 0) {
+      const float e = ltot > 0.f ? mrow + log2f(ltot) : kNegInf;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(e), lrsrc, (int)(orow * 4u), 0, kStoreDevice);
+    }
+  }
+  if (!p.fused_merge) return;
+
+  // ---- merge by the split that arrives last ----
+  // The partials were written through to device scope (sc1); once every
+  // wave's stores are complete, a device-scope arrival count publishes them.
+  // No release fence is needed for that (it would write back the whole L2 of
+  // this XCD in every workgroup); only the merging workgroup acquires, and it
+  // reads the partials with device-scope loads.
+  wait_copies();    // this wave's partial stores are complete
+  __syncthreads();  // ... and every wave's
+  if (tid == 0) {
+    int32_t* ctr = p.counters + (b * Hkv + kvh);
+    const int old = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int is_last = old == NS - 1;
+    if (is_last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *last_sh = is_last;
+  }
+  __syncthreads();
+  if (!*last_sh) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  // Every split's partial of this (sequence, KV head): item = (row m < M, 8
+  // dims); T threads share an item, thread `sub` of them taking splits sub,
+  // sub + T, ... (the host guarantees at most kDecMergeLoads each), all of
+  // whose loads are issued before any is used, so the merge costs one memory
+  // round trip. The T partial merges are then combined in LDS, in a fixed
+  // order (results do not depend on which split arrived last).
+  const int items = M * (D / 8);
+  const int T = items >= 256 ? 1 : 256 / items;
+  const int item = tid / T, sub = tid % T;
+  const size_t split_rows = (size_t)p.B * a_R * Hq;
+  const __amdgpu_buffer_rsrc_t prsrc = make_rsrc(p.part_o, 0xFFFFFFFFu);
+  const __amdgpu_buffer_rsrc_t plsrc = make_rsrc(p.part_lse, 0xFFFFFFFFu);
+  typedef __attribute__((address_space(3))) float lds_f32;
+  lds_f32* const red = reinterpret_cast<lds_f32*>(vb);  // [T][256 / T][10] partial merges
+  for (int it0 = 0; it0 < items; it0 += 256 / T) {
+    const int it = it0 + item;
+    const bool live = it < items;
+    const int m = live ? it / (D / 8) : 0, d = live ? (it % (D / 8)) * 8 : 0;
+    const int r = m / g;
+    const uint32_t orow = (uint32_t)((b * a_R + r) * Hq + kvh * g + (m - r * g));
+    float e[kDecMergeLoads];
+    u32x4 raw[kDecMergeLoads];
+#pragma unroll
+    for (int j = 0; j < kDecMergeLoads; ++j) {
+      const int sj = sub + j * T;
+      const bool in = live && sj < NS;
+      const uint32_t prow = (uint32_t)((size_t)(in ? sj : 0) * split_rows + orow);
+      e[j] = in ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(plsrc, (int)(prow * 4u), 0, kStoreDevice))
+                : kNegInf;
+      raw[j] = in ? __builtin_amdgcn_raw_buffer_load_b128(prsrc, (int)(prow * (uint32_t)(2 * D) + 2u * d), 0,
+                                                          kStoreDevice)
+                  : u32x4{0u, 0u, 0u, 0u};
+    }
+    float emax = kNegInf;
+#pragma unroll
+    for (int j = 0; j < kDecMergeLoads; ++j) emax = fmaxf(emax, e[j]);
+    float wsum = 0.f, acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    if (emax != kNegInf) {
+#pragma unroll
+      for (int j = 0; j < kDecMergeLoads; ++j) {
+        const float wgt = __builtin_amdgcn_exp2f(e[j] - emax);  // 0 for an empty or absent split
+        wsum += wgt;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] = fmaf(__uint_as_float(raw[j][i] << 16), wgt, acc[2 * i]);
+          acc[2 * i + 1] = fmaf(__uint_as_float(raw[j][i] & 0xffff0000u), wgt, acc[2 * i + 1]);
+        }
+      }
+    }
+    if (T > 1) {
+      __syncthreads();  // the previous round's reads of `red` are done
+      lds_f32* slot = red + ((size_t)sub * (256 / T) + item) * 10;
+      slot[0] = emax;
+      slot[1] = wsum;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) slot[2 + i] = acc[i];
+      __syncthreads();
+      if (sub != 0) continue;
+      // thread 0 of the item folds the others in, in order
+      for (int q = 1; q < T; ++q) {
+        const lds_f32* o2 = red + ((size_t)q * (256 / T) + item) * 10;
+        const float e2 = o2[0];
+        const float mx = fmaxf(emax, e2);
+        if (mx == kNegInf) continue;
+        const float a1 = __builtin_amdgcn_exp2f(emax - mx), a2 = __builtin_amdgcn_exp2f(e2 - mx);
+        wsum = wsum * a1 + o2[1] * a2;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = acc[i] * a1 + o2[2 + i] * a2;
+        emax = mx;
+      }
+    }
+    if (!live) continue;
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    u32x4 pk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      pk[i] = (uint32_t)f32_to_bf16_bits(acc[2 * i] * inv) | ((uint32_t)f32_to_bf16_bits(acc[2 * i + 1] * inv) << 16);
+    *reinterpret_cast<u32x4*>(reinterpret_cast<u16*>(p.out) + (size_t)orow * D + d) = pk;
+    if (p.lse && d == 0) p.lse[orow] = (emax + log2f(wsum)) * 0.69314718055994531f;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_dec_kernel(
+    const int32_t* __restrict__ a_len, const void* __restrict__ a_q, const void* __restrict__ a_kc,
+    const void* __restrict__ a_vc, uint32_t a_hkv_g, uint32_t a_k_bl, int a_R, int a_ns, int a_cap,
+    int a_max_len, int a_nwg, AttnParams p) {
+  using L = Lay<D>;
+  static_assert(D == 128, "the decode kernel is built for head_dim 128");
+  static_assert(4 * 2 * 4 * 1024 <= 2 * L::TILE_BYTES, "P does not fit over the K tiles");
+  __shared__ __attribute__((aligned(1024))) uint8_t kb[2 * L::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t vb[2 * L::TILE_BYTES];
+  __shared__ float rmax[4][2][32];  // log2-domain row maxima per (row tile, key tile)
+  __shared__ float rsum[4][2][32];  // row sums (of the rounded P) per (row tile, key tile)
+  __shared__ int last_sh;
+  const int Hkv = (int)(a_hkv_g & 0xffff), g = (int)(a_hkv_g >> 16);
+  const int kdr = (int)(a_k_bl & 0xffff), bl = (int)(a_k_bl >> 16);
+  const int NS = a_ns;
+  int w = remap_xcd((int)__builtin_amdgcn_workgroup_id_x(), a_nwg);
+  const int s = w % NS;
+  w /= NS;
+  const int kvh = w % Hkv;
+  const int b = w / Hkv;
+  attn_dec_body<D>((lds_u8*)kb, (lds_u8*)vb, rmax, rsum, &last_sh, a_len, a_q, a_kc, a_vc, a_R, a_cap, a_max_len, b,
+                   kvh, s, NS, Hkv, g, kdr, bl, p);
+}
+
+// ---------------------------------------------------------------------------
 // fp32 path: one wave per (packed query row, split). Plain VALU arithmetic in
 // fp32 with an online softmax in the log2 domain; same split/merge scheme.
 // ---------------------------------------------------------------------------
@@ -1009,12 +1350,37 @@ AttnPlan plan_attn(int dtype, int B, int Hq, int Hkv, int D, int R, int max_len,
   const int g = Hq / Hkv;
   const long M = (long)R * g;
   long base;
-  if (dtype == 1) {
-    // 32 or 64 query rows per wave; TIDAR_ATTN_WAVE_ROWS overrides the choice (tuning knob)
+  // Decode regime (few packed rows per KV head): a latency-bound kernel that
+  // copies a whole split into LDS at once, selected by TIDAR_ATTN_DECODE=1.
+  // Measured on MI355X it is not faster than the main kernel at these sizes
+  // (both sit near the floor of a launch plus dependent memory round trips),
+  // so the main kernel stays the default. TIDAR_ATTN_FUSED_MERGE=0/1 forces
+  // the merge kernel / the in-kernel merge (the latter within its load bound).
+  const char* dec_env = getenv("TIDAR_ATTN_DECODE");
+  if (dtype == 1 && D == 128 && M <= kDecMaxRows && R <= 128 && forced_splits == 0 && dec_env && atoi(dec_env) == 1) {
+    pl.decode = 1;
     pl.nqt = 1;
     pl.waves = 4;
-    if (const char* e = getenv("TIDAR_ATTN_WAVE_ROWS")) pl.nqt = atoi(e) >= 64 ? 2 : 1;
-    if (const char* e = getenv("TIDAR_ATTN_WAVES")) pl.waves = (atoi(e) == 8 && pl.nqt == 1) ? 8 : 4;
+    pl.bm = kBM;
+    pl.qtiles = 1;
+    pl.chunk = kDecChunk;
+    pl.S = (max_len + kDecChunk - 1) / kDecChunk + 1;  // prefix splits, then the step keys
+    const long items = M * (D / 8);
+    const long T = items >= 256 ? 1 : 256 / items;
+    const bool fits = (pl.S + T - 1) / T <= kDecMergeLoads;
+    pl.fused_merge = fits && M <= 32;
+    if (const char* e = getenv("TIDAR_ATTN_FUSED_MERGE")) pl.fused_merge = fits && atoi(e) != 0;
+    pl.counter_bytes = ((size_t)B * Hkv * sizeof(int32_t) + 255) / 256 * 256;
+    const size_t prow = (size_t)pl.S * B * R * Hq;
+    pl.ws_bytes = pl.counter_bytes + (prow * D * 2 + 255) / 256 * 256 + prow * sizeof(float);
+    return pl;
+  }
+  if (dtype == 1) {
+    // 32 query rows per wave, four waves; TIDAR_ATTN_WAVES=8 selects 8-wave
+    // workgroups of 256 rows (a tuning knob, built for head_dim 128 only)
+    pl.nqt = 1;
+    pl.waves = 4;
+    if (const char* e = getenv("TIDAR_ATTN_WAVES")) pl.waves = (atoi(e) == 8 && D == 128) ? 8 : 4;
     pl.bm = pl.waves == 8 ? 2 * kBM : kBM;
     pl.qtiles = (int)((M + pl.bm - 1) / pl.bm);
     base = (long)B * Hkv * pl.qtiles;
@@ -1084,6 +1450,18 @@ AttnPlan plan_attn(int dtype, int B, int Hq, int Hkv, int D, int R, int max_len,
 }
 
 hipError_t launch_attn_bf16(const AttnParams& p, hipStream_t stream) {
+  if (p.decode) {
+    const size_t grid = (size_t)p.B * p.Hkv * p.S;
+    if (grid > 0x7fffffff || p.Hkv > 0xffff || p.g > 0xffff || p.k > 0xffff || p.block_len > 0xffff || p.D != 128)
+      return hipErrorInvalidValue;
+    const uint32_t hkv_g = (uint32_t)p.Hkv | ((uint32_t)p.g << 16);
+    const uint32_t k_bl = (uint32_t)p.k | ((uint32_t)p.block_len << 16);
+    hipLaunchKernelGGL(attn_dec_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream, p.cache_len, p.q, p.k_cache,
+                       p.v_cache, hkv_g, k_bl, p.R, p.S, p.cap, p.max_len, (int)grid, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.fused_merge) return e;
+    return launch_merge(p, true, stream);
+  }
   const size_t grid = (size_t)p.B * p.Hkv * p.qtiles * p.S;
   if (grid > 0x7fffffff || p.qtiles > 0xffff || p.S > 0xffff || p.Hkv > 0xffff || p.g > 0xffff || p.k > 0xffff ||
       p.block_len > 0xffff)
@@ -1093,17 +1471,13 @@ hipError_t launch_attn_bf16(const AttnParams& p, hipStream_t stream) {
   const uint32_t k_bl = (uint32_t)p.k | ((uint32_t)p.block_len << 16);
 #define TIDAR_ATTN_ARGS                                                                                       \
   p.cache_len, p.q, p.k_cache, qt_s, hkv_g, k_bl, p.R, (int)grid, p.cap, p.chunk, p.max_len, p
-  // 128 query rows per workgroup: four waves of 32 rows, or two of 64
-  if (p.D == 128 && p.nqt == 1 && p.waves == 8)
+  // 128 query rows per workgroup (four waves of 32 rows), or 256 (eight waves, head_dim 128)
+  if (p.D == 128 && p.waves == 8)
     hipLaunchKernelGGL((attn_bf16_kernel<128, 1, 8>), dim3((unsigned)grid), dim3(512), 0, stream, TIDAR_ATTN_ARGS);
-  else if (p.D == 128 && p.nqt == 1)
+  else if (p.D == 128 && p.waves == 4)
     hipLaunchKernelGGL((attn_bf16_kernel<128, 1, 4>), dim3((unsigned)grid), dim3(256), 0, stream, TIDAR_ATTN_ARGS);
-  else if (p.D == 128 && p.nqt == 2)
-    hipLaunchKernelGGL((attn_bf16_kernel<128, 2, 2>), dim3((unsigned)grid), dim3(128), 0, stream, TIDAR_ATTN_ARGS);
-  else if (p.D == 64 && p.nqt == 1)
+  else if (p.D == 64 && p.waves == 4)
     hipLaunchKernelGGL((attn_bf16_kernel<64, 1, 4>), dim3((unsigned)grid), dim3(256), 0, stream, TIDAR_ATTN_ARGS);
-  else if (p.D == 64 && p.nqt == 2)
-    hipLaunchKernelGGL((attn_bf16_kernel<64, 2, 2>), dim3((unsigned)grid), dim3(128), 0, stream, TIDAR_ATTN_ARGS);
   else
     return hipErrorInvalidValue;
 #undef TIDAR_ATTN_ARGS

@@ -23,12 +23,17 @@ struct AttnParams {
   // log-sum-exp in the log2 domain, [S, B, R, Hq] fp32 (-inf: no visible key)
   void* part_o;
   float* part_lse;
+  // decode path: arrival counters, one per (sequence, KV head), zero between
+  // launches (the last-arriving split merges and resets its counter)
+  int32_t* counters;
   int B, Hq, Hkv, D, g, R, k, num_blocks, block_len, cap, max_len;
   int S;          // number of prefix splits
   int chunk;      // prefix keys per split
   int qtiles;     // query tiles per (b, kv head)
   int nqt;        // 32-row query tiles per wave (bf16 path)
   int waves;      // waves per workgroup (bf16 path)
+  int decode;     // 1: the decode-regime kernel (few packed rows per KV head)
+  int fused_merge;  // decode path: the last-arriving split merges (no merge kernel)
   float sm_scale;
   float scale_log2;  // sm_scale * log2(e)
 };
@@ -40,7 +45,10 @@ struct AttnPlan {
   int nqt;
   int waves;
   int bm;          // packed query rows per workgroup
+  int decode;      // decode-regime kernel: S prefix splits of `chunk` keys plus one split of step keys
+  int fused_merge;
   size_t ws_bytes;
+  size_t counter_bytes;  // decode path: leading workspace bytes holding the arrival counters
 };
 
 AttnPlan plan_attn(int dtype, int B, int Hq, int Hkv, int D, int R, int max_len, int forced_splits,

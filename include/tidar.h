@@ -96,7 +96,10 @@ int tidar_version(void);
  * separately and merged by log-sum-exp; the result does not depend on the
  * split count beyond floating-point rounding. Each split's normalised output
  * is held in the workspace in the input precision (bf16 or fp32), with its
- * log-sum-exp in fp32.
+ * log-sum-exp in fp32. An optional decode-regime kernel (few packed query
+ * rows per KV head, see tidar_attn_workspace_bytes) streams 128-key splits
+ * plus one split of the step's keys, and the split that finishes last merges
+ * them when they are small enough.
  * ---------------------------------------------------------------------- */
 typedef struct {
   int32_t batch;           /* B >= 1 */
@@ -113,7 +116,13 @@ typedef struct {
   int32_t num_splits;      /* 0 = library chooses; otherwise the prefix split count */
 } tidar_attn_desc;
 
-/* Workspace bytes tidar_attn_step needs for this descriptor (0 if none). */
+/* Workspace bytes tidar_attn_step needs for this descriptor (0 if none).
+ * The workspace must be zero-filled before its first use (hipMemset, or
+ * torch.zeros): when the decode-regime kernel is selected (environment
+ * TIDAR_ATTN_DECODE=1, and few packed query rows per KV head: Hq/Hkv * R <=
+ * 128, R <= 128, head_dim 128, bf16, num_splits = 0) its leading bytes hold
+ * one arrival counter per (sequence, KV head), which every launch returns to
+ * zero. A workspace that only ever serves other launches needs no clearing. */
 size_t tidar_attn_workspace_bytes(const tidar_attn_desc* desc);
 
 /*

@@ -148,3 +148,20 @@ def test_logprob_rejects_bad_arguments():
     assert need >= 4 * 38 * 8 and call(wsb=need - 1) == _lib.TIDAR_E_WORKSPACE
     assert call(ws=FAKE + 16) == _lib.TIDAR_E_INVALID
     assert lib.tidar_logprob_workspace_bytes(0, 10) == 0
+
+
+def test_decode_regime_workspace_layout(monkeypatch):
+    """With TIDAR_ATTN_DECODE=1, few packed rows per KV head select the decode
+    kernel: 128-key prefix splits plus one split of step keys, arrival
+    counters first (256-byte padded), then the bf16 split outputs and fp32
+    split log-sum-exps."""
+    monkeypatch.setenv("TIDAR_ATTN_DECODE", "1")
+    d = _desc(num_q_heads=64, num_kv_heads=8, k=1, num_blocks=0, block_len=1, cache_capacity=4104,
+              max_cache_len=4096)
+    S, rows = 4096 // 128 + 1, 1 * 1 * 64
+    expect = 256 + (S * rows * 128 * 2 + 255) // 256 * 256 + S * rows * 4
+    assert lib.tidar_attn_workspace_bytes(ctypes.byref(d)) == expect
+    # forcing a split count keeps the main kernel (no counters)
+    f = _desc(num_q_heads=64, num_kv_heads=8, k=1, num_blocks=0, block_len=1, cache_capacity=4104,
+              max_cache_len=4096, num_splits=4)
+    assert lib.tidar_attn_workspace_bytes(ctypes.byref(f)) == 4 * rows * 128 * 2 + 4 * rows * 4

@@ -53,8 +53,11 @@ def test_config2_bf16(seed):
 @pytest.mark.parametrize("waves", ["8"])
 def test_workgroup_shape_knob_matches_oracle(waves, monkeypatch):
     """The 8-wave workgroup layout (a tuning knob, TIDAR_ATTN_WAVES) gives the
-    same results within tolerance, including a half-filled last query tile."""
+    same results within tolerance, including a half-filled last query tile
+    (the decode-regime kernel is switched off, as by default, so the small case runs it too),
+    and head_dim 64, which the knob leaves on four waves."""
     monkeypatch.setenv("TIDAR_ATTN_WAVES", waves)
+    monkeypatch.setenv("TIDAR_ATTN_DECODE", "0")
     c = config_attn(2, seed=5)
     out, lse = run_attn(c)
     ref, rlse = _oracle_full(c)
@@ -65,6 +68,12 @@ def test_workgroup_shape_knob_matches_oracle(waves, monkeypatch):
     out2, _ = run_attn(small)
     ref2, _ = _oracle_full(small)
     assert _report(f"small bf16 waves={waves}", out2, ref2, TOL["bf16"]) <= TOL["bf16"]
+    d64 = attn_case(dtype="bf16", layers=1, batch=1, num_q_heads=8, num_kv_heads=1, head_dim=64, k=16,
+                    num_blocks=17, block_len=16, cache_len=[333], cache_capacity=350, seed=7)
+    out3, _ = run_attn(d64)
+    ref3, _ = _oracle_full(d64)
+    assert np.isfinite(out3).all()
+    assert _report(f"D=64 bf16 waves={waves}", out3, ref3, TOL["bf16"]) <= TOL["bf16"]
 
 
 SMALL = [

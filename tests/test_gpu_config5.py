@@ -66,7 +66,7 @@ def test_config5_ragged_full_depth_64_steps():
     rel = np.zeros(B, np.int32)                      # committed rows past P0_b
     gen = torch.Generator(device="cuda").manual_seed(1234)
 
-    committed, acc_flips, draw_flips, checked_layers = [], 0, 0, set()
+    committed, acc_flips, draw_flips, checked_layers, n_checks = [], 0, 0, set(), 0
     for it in range(steps):
         for t in (step.q, step.k_step, step.v_step):
             t.copy_(torch.randn(t.shape, generator=gen, device="cuda", dtype=torch.float32))
@@ -85,7 +85,8 @@ def test_config5_ragged_full_depth_64_steps():
         # attention on sampled rows of four layers, against the oracle's view of the cache
         if it % 8 == 0 or it == steps - 1:
             srng = np.random.default_rng(1000 + it)
-            for layer in ((4 * (it // 8) + j) % L for j in range(4)):
+            n_checks += 1
+            for layer in ((4 * (n_checks - 1) + j) % L for j in range(4)):
                 checked_layers.add(layer)
                 kc = _f32(_bits(k0[layer]))
                 vc = _f32(_bits(v0[layer]))
