@@ -36,6 +36,7 @@ EXPORTS = (
     "tidar_status_string", "tidar_last_error", "tidar_version",
     "tidar_attn_workspace_bytes", "tidar_attn_step", "tidar_kv_commit",
     "tidar_reject_workspace_bytes", "tidar_reject_sample", "tidar_reject_sample_trust",
+    "tidar_reject_sample_noalloc", "tidar_reject_noalloc_max_bytes",
     "tidar_logprob_workspace_bytes", "tidar_token_logprobs",
     # measurement kernels (include/tidar_ceilings.h)
     "tidar_ceiling_hbm_read", "tidar_ceiling_mfma_bf16", "tidar_ceiling_exp_f32", "tidar_ceiling_fma_f32",
@@ -86,6 +87,11 @@ def load() -> ctypes.CDLL:
     lib.tidar_reject_sample_trust.restype = ctypes.c_int
     lib.tidar_reject_sample_trust.argtypes = [i32, i32, i32, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float,
                                               vp, vp, vp, vp, vp, sz, vp]
+    lib.tidar_reject_sample_noalloc.restype = ctypes.c_int
+    lib.tidar_reject_sample_noalloc.argtypes = [i32, i32, i32, vp, vp, vp, vp, ctypes.c_float, ctypes.c_float,
+                                                vp, vp, vp, vp, vp]
+    lib.tidar_reject_noalloc_max_bytes.restype = sz
+    lib.tidar_reject_noalloc_max_bytes.argtypes = []
     lib.tidar_ceiling_hbm_read.restype = ctypes.c_int
     lib.tidar_ceiling_hbm_read.argtypes = [vp, sz, ctypes.c_int, vp, vp]
     for name in ("tidar_ceiling_mfma_bf16", "tidar_ceiling_exp_f32", "tidar_ceiling_fma_f32"):
@@ -220,6 +226,24 @@ def reject_sample(*, ar_logits, diff_logits, drafts, uniforms, accept_len, next_
     else:
         _check(_lib.tidar_reject_sample_trust(B, k, V, _ptr(ar_logits), _ptr(diff_logits), _ptr(drafts),
                                               _ptr(uniforms), float(temperature), float(trust_ar), *args))
+
+
+def reject_sample_noalloc(*, ar_logits, diff_logits, drafts, uniforms, accept_len, next_token, ratio=None,
+                          dev_status=None, temperature: float = 1.0, trust_ar: float = 1.0, stream=None):
+    """tidar_reject_sample_noalloc: the sampler on the library's static scratch (no workspace)."""
+    B, kp1, V = ar_logits.shape
+    k = kp1 - 1
+    _dev(ar_logits, torch.float32, "ar_logits")
+    _dev(diff_logits, torch.float32, "diff_logits", allow_none=(k == 0))
+    _dev(drafts, torch.int32, "drafts", allow_none=(k == 0))
+    _dev(uniforms, torch.float32, "uniforms")
+    _dev(accept_len, torch.int32, "accept_len")
+    _dev(next_token, torch.int32, "next_token")
+    _dev(ratio, torch.float32, "ratio", allow_none=True)
+    _dev(dev_status, torch.int32, "dev_status", allow_none=True)
+    _check(_lib.tidar_reject_sample_noalloc(B, k, V, _ptr(ar_logits), _ptr(diff_logits), _ptr(drafts),
+                                            _ptr(uniforms), float(temperature), float(trust_ar), _ptr(accept_len),
+                                            _ptr(next_token), _ptr(ratio), _ptr(dev_status), _stream(stream)))
 
 
 def logprob_workspace_bytes(rows: int, vocab: int) -> int:

@@ -90,6 +90,69 @@ int check_desc(const tidar_attn_desc* d, tidar::AttnPlan* plan) {
   return TIDAR_OK;
 }
 
+// Shared by the sampler entry points. With noalloc the workspace is the
+// library's static device scratch (no caller buffer, no allocation).
+int reject_common(int32_t batch, int32_t k, int32_t vocab, const float* ar_logits, const float* diff_logits,
+                  const int32_t* drafts, const float* uniforms, float temperature, float trust_ar,
+                  int32_t* accept_len, int32_t* next_token, float* ratio, int32_t* dev_status, void* workspace,
+                  size_t workspace_bytes, bool noalloc, void* stream) {
+  if (batch < 1 || k < 0 || vocab < 1) return fail(TIDAR_E_INVALID, "need batch >= 1, k >= 0, vocab >= 1");
+  if (k > tidar::reject_max_k()) return fail(TIDAR_E_UNSUPPORTED, "k = %d exceeds %d", k, tidar::reject_max_k());
+  tidar::RejectParams p{};
+  p.B = batch;
+  p.k = k;
+  p.V = vocab;
+  tidar::plan_reject(p);
+  if (p.nchunks > tidar::reject_max_chunks())
+    return fail(TIDAR_E_UNSUPPORTED, "vocab %d too large (max %d)", vocab, tidar::reject_max_chunks() * p.chunk);
+  if ((long)batch * (k + 1) * (long)vocab > 0x7fffffffL || (long)batch * (2 * k + 1) * p.nchunks > 0x7fffffffL)
+    return fail(TIDAR_E_UNSUPPORTED, "logits too large");
+  if (!(temperature > 0.f) || !isfinite(temperature)) return fail(TIDAR_E_INVALID, "temperature must be > 0");
+  if (!(trust_ar >= 0.f && trust_ar <= 1.f)) return fail(TIDAR_E_INVALID, "trust_ar must lie in [0, 1]");
+  if (!ar_logits || !uniforms || !accept_len || !next_token)
+    return fail(TIDAR_E_INVALID, "a required pointer is NULL");
+  if (k > 0 && (!diff_logits || !drafts)) return fail(TIDAR_E_INVALID, "diff_logits and drafts required when k > 0");
+  if (!aligned(ar_logits, 16) || (diff_logits && !aligned(diff_logits, 16)))
+    return fail(TIDAR_E_INVALID, "logit pointers must be 16-byte aligned");
+  const size_t need = tidar::reject_workspace_bytes(batch, k, vocab);
+  if (noalloc) {
+    if (need > tidar::kRejectScratchBytes)
+      return fail(TIDAR_E_WORKSPACE, "batch %d, k %d, vocab %d need %zu bytes of scratch; the allocation-free "
+                  "sampler holds %zu", batch, k, vocab, need, tidar::kRejectScratchBytes);
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "device of the stream");
+    if ((e = tidar::reject_scratch(dev, &workspace)) != hipSuccess) return hip_fail(e, "sampler scratch address");
+    workspace_bytes = tidar::kRejectScratchBytes;
+  }
+  if (!workspace || workspace_bytes < need)
+    return fail(TIDAR_E_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
+  if (!aligned(workspace, 256)) return fail(TIDAR_E_INVALID, "workspace must be 256-byte aligned");
+  p.ar = ar_logits;
+  p.diff = diff_logits;
+  p.drafts = drafts;
+  p.uniforms = uniforms;
+  p.inv_temp = 1.f / temperature;
+  p.mix = trust_ar == 1.f ? 0 : trust_ar == 0.f ? 2 : 1;
+  p.lam = trust_ar;
+  p.mu = 1.f - trust_ar;
+  p.accept_len = accept_len;
+  p.next_token = next_token;
+  p.ratio = ratio;
+  p.dev_status = dev_status;
+  char* ws = static_cast<char*>(workspace);
+  const size_t a = ((size_t)batch * (2 * k + 1) * p.nchunks * sizeof(float2) + 255) / 256 * 256;
+  const size_t bsz = ((size_t)2 * batch * p.nchunks * sizeof(double) + 255) / 256 * 256;
+  p.row_stats = reinterpret_cast<float2*>(ws);
+  p.resid_sums = reinterpret_cast<double*>(ws + a);
+  p.decision = reinterpret_cast<int32_t*>(ws + a + bsz);
+  const size_t dsz = ((size_t)batch * 2 * sizeof(int32_t) + 255) / 256 * 256;
+  p.row_mz = reinterpret_cast<float2*>(ws + a + bsz + dsz);
+  hipError_t e = tidar::launch_reject(p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "reject launch");
+  return TIDAR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -246,52 +309,19 @@ int tidar_reject_sample_trust(int32_t batch, int32_t k, int32_t vocab, const flo
                               float temperature, float trust_ar, int32_t* accept_len, int32_t* next_token,
                               float* ratio, int32_t* dev_status, void* workspace, size_t workspace_bytes,
                               void* stream) {
-  if (batch < 1 || k < 0 || vocab < 1) return fail(TIDAR_E_INVALID, "need batch >= 1, k >= 0, vocab >= 1");
-  if (k > tidar::reject_max_k()) return fail(TIDAR_E_UNSUPPORTED, "k = %d exceeds %d", k, tidar::reject_max_k());
-  tidar::RejectParams p{};
-  p.B = batch;
-  p.k = k;
-  p.V = vocab;
-  tidar::plan_reject(p);
-  if (p.nchunks > tidar::reject_max_chunks())
-    return fail(TIDAR_E_UNSUPPORTED, "vocab %d too large (max %d)", vocab, tidar::reject_max_chunks() * p.chunk);
-  if ((long)batch * (k + 1) * (long)vocab > 0x7fffffffL || (long)batch * (2 * k + 1) * p.nchunks > 0x7fffffffL)
-    return fail(TIDAR_E_UNSUPPORTED, "logits too large");
-  if (!(temperature > 0.f) || !isfinite(temperature)) return fail(TIDAR_E_INVALID, "temperature must be > 0");
-  if (!(trust_ar >= 0.f && trust_ar <= 1.f)) return fail(TIDAR_E_INVALID, "trust_ar must lie in [0, 1]");
-  if (!ar_logits || !uniforms || !accept_len || !next_token)
-    return fail(TIDAR_E_INVALID, "a required pointer is NULL");
-  if (k > 0 && (!diff_logits || !drafts)) return fail(TIDAR_E_INVALID, "diff_logits and drafts required when k > 0");
-  if (!aligned(ar_logits, 16) || (diff_logits && !aligned(diff_logits, 16)))
-    return fail(TIDAR_E_INVALID, "logit pointers must be 16-byte aligned");
-  const size_t need = tidar::reject_workspace_bytes(batch, k, vocab);
-  if (!workspace || workspace_bytes < need)
-    return fail(TIDAR_E_WORKSPACE, "workspace %zu bytes < required %zu", workspace_bytes, need);
-  if (!aligned(workspace, 256)) return fail(TIDAR_E_INVALID, "workspace must be 256-byte aligned");
-  p.ar = ar_logits;
-  p.diff = diff_logits;
-  p.drafts = drafts;
-  p.uniforms = uniforms;
-  p.inv_temp = 1.f / temperature;
-  p.mix = trust_ar == 1.f ? 0 : trust_ar == 0.f ? 2 : 1;
-  p.lam = trust_ar;
-  p.mu = 1.f - trust_ar;
-  p.accept_len = accept_len;
-  p.next_token = next_token;
-  p.ratio = ratio;
-  p.dev_status = dev_status;
-  char* ws = static_cast<char*>(workspace);
-  const size_t a = ((size_t)batch * (2 * k + 1) * p.nchunks * sizeof(float2) + 255) / 256 * 256;
-  const size_t bsz = ((size_t)2 * batch * p.nchunks * sizeof(double) + 255) / 256 * 256;
-  p.row_stats = reinterpret_cast<float2*>(ws);
-  p.resid_sums = reinterpret_cast<double*>(ws + a);
-  p.decision = reinterpret_cast<int32_t*>(ws + a + bsz);
-  const size_t dsz = ((size_t)batch * 2 * sizeof(int32_t) + 255) / 256 * 256;
-  p.row_mz = reinterpret_cast<float2*>(ws + a + bsz + dsz);
-  hipError_t e = tidar::launch_reject(p, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "reject launch");
-  return TIDAR_OK;
+  return reject_common(batch, k, vocab, ar_logits, diff_logits, drafts, uniforms, temperature, trust_ar, accept_len,
+                       next_token, ratio, dev_status, workspace, workspace_bytes, false, stream);
 }
+
+int tidar_reject_sample_noalloc(int32_t batch, int32_t k, int32_t vocab, const float* ar_logits,
+                                const float* diff_logits, const int32_t* drafts, const float* uniforms,
+                                float temperature, float trust_ar, int32_t* accept_len, int32_t* next_token,
+                                float* ratio, int32_t* dev_status, void* stream) {
+  return reject_common(batch, k, vocab, ar_logits, diff_logits, drafts, uniforms, temperature, trust_ar, accept_len,
+                       next_token, ratio, dev_status, nullptr, 0, true, stream);
+}
+
+size_t tidar_reject_noalloc_max_bytes(void) { return tidar::kRejectScratchBytes; }
 
 
 size_t tidar_logprob_workspace_bytes(int32_t rows, int32_t vocab) {

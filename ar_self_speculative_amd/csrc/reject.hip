@@ -27,6 +27,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 namespace tidar {
 namespace {
 
@@ -482,6 +484,48 @@ __global__ __launch_bounds__(kThreads) void rej_pick_kernel(const int32_t* __res
 }
 
 }  // namespace
+
+// Scratch of the allocation-free entry point: the sampler's workspace (per
+// (row, chunk) statistics, per-chunk draw masses, the decision, merged row
+// statistics) lives in this file-scope device array instead of a caller
+// buffer. Each GPU holds its own copy for the life of the process. Host code
+// never passes the array's name to a kernel (on the host it is only a
+// stand-in); it passes the device address hipGetSymbolAddress returns,
+// looked up once per device with that device current.
+}  // namespace tidar
+
+static __device__ __align__(256) unsigned char scratch[tidar::kRejectScratchBytes];
+
+namespace tidar {
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t reject_scratch(int device, void** out) {
+  *out = nullptr;
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[device]) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != device) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[device] = ptr;
+  }
+  *out = g_scratch_ptr[device];
+  return hipSuccess;
+}
 
 size_t reject_workspace_bytes(int B, int k, int V) {
   const size_t nchunks = ((size_t)V + kChunk - 1) / kChunk;

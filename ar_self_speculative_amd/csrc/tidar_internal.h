@@ -92,6 +92,10 @@ struct RejectParams {
   float2* row_mz;       // [B, 2k+1] merged (max, sum exp) of every row
 };
 size_t reject_workspace_bytes(int B, int k, int V);
+// Size of the device-resident scratch behind tidar_reject_sample_noalloc, and
+// its address on `device` (looked up once per device, then cached).
+constexpr size_t kRejectScratchBytes = size_t(1) << 20;
+hipError_t reject_scratch(int device, void** out);
 int reject_max_k();
 int reject_max_chunks();
 void plan_reject(RejectParams& p);

@@ -218,6 +218,32 @@ int tidar_reject_sample_trust(int32_t batch, int32_t k, int32_t vocab, const flo
                               size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * The sampler with no workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Arguments, layouts, results and errors
+ * are those of tidar_reject_sample_trust (trust_ar = 1 is
+ * tidar_reject_sample); it runs the same kernels and gives the same bits.
+ * The workspace is a static device array inside the library, of
+ * tidar_reject_noalloc_max_bytes() bytes (1 MiB) per GPU, held until the
+ * process ends; its device address is looked up once per device, on the
+ * first call there. Calls whose tidar_reject_workspace_bytes(batch, k,
+ * vocab) exceeds that size return TIDAR_E_WORKSPACE before any launch
+ * (1 MiB covers e.g. batch 64 at k = 16, vocab 151936). No allocation and no
+ * allocating library routine is called. Every call on one GPU uses the same
+ * array and overwrites all of it that it reads, so nothing needs clearing;
+ * calls that overlap on one GPU (different streams, or host threads)
+ * race on it and must be serialised by the caller. The stream's device is
+ * the GPU used (NULL stream: the current device).
+ * ---------------------------------------------------------------------- */
+int tidar_reject_sample_noalloc(int32_t batch, int32_t k, int32_t vocab, const float* ar_logits,
+                                const float* diff_logits, const int32_t* drafts, const float* uniforms,
+                                float temperature, float trust_ar, int32_t* accept_len,
+                                int32_t* next_token, float* ratio, int32_t* dev_status, void* stream);
+
+/* Bytes of the static scratch behind tidar_reject_sample_noalloc. */
+size_t tidar_reject_noalloc_max_bytes(void);
+
+/* ------------------------------------------------------------------------
  * Likelihood mode: per-token AR log-probabilities (talk notes on
  * notes.yuuk.io, 尤度評価: with the attention mask set to causal, TiDAR
  * scores a sequence as an AR model in one forward, no Monte-Carlo sampling;

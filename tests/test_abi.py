@@ -150,6 +150,21 @@ def test_logprob_rejects_bad_arguments():
     assert lib.tidar_logprob_workspace_bytes(0, 10) == 0
 
 
+def test_noalloc_sampler_rejects_inputs_beyond_its_scratch():
+    """The allocation-free sampler checks its static scratch size on the host,
+    before any HIP call: a shape that needs more returns TIDAR_E_WORKSPACE."""
+    cap = int(lib.tidar_reject_noalloc_max_bytes())
+    assert cap == 1 << 20
+    B, k, V = 64, 128, 151936
+    assert _lib.reject_workspace_bytes(B, k, V) > cap
+    st = lib.tidar_reject_sample_noalloc(B, k, V, FAKE, FAKE, FAKE, FAKE, 1.0, 1.0, FAKE, FAKE, None, None, None)
+    assert st == _lib.TIDAR_E_WORKSPACE
+    assert b"scratch" in lib.tidar_last_error()
+    # and the ordinary argument checks come first
+    assert lib.tidar_reject_sample_noalloc(B, k, V, FAKE, FAKE, FAKE, FAKE, 0.0, 1.0, FAKE, FAKE, None, None,
+                                           None) == _lib.TIDAR_E_INVALID
+
+
 def test_decode_regime_workspace_layout(monkeypatch):
     """With TIDAR_ATTN_DECODE=1, few packed rows per KV head select the decode
     kernel: 128-key prefix splits plus one split of step keys, arrival
