@@ -396,19 +396,58 @@ def likelihood_bench(args) -> None:
     }), flush=True)
 
 
+def knee_ceilings() -> dict:
+    """The two ceilings the free-slot knee is computed from, measured on this machine:
+    HBM streaming-read bandwidth and the bf16 MFMA rate (ceilings_bench's kernels)."""
+    import torch
+
+    import ar_self_speculative_amd as tidar
+
+    sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+
+    def best(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e-3)
+        return min(ts)
+
+    hbm = max(nbytes / best(lambda: tidar.ceiling("hbm_read", buf, grid, sink)) / 1e9 for grid in (4096, 8192))
+    del buf
+    grid, iters = 1024, 20000
+    mfma = grid * 4 * 4 * iters * 32768 / best(lambda: tidar.ceiling("mfma_bf16", grid, iters, sink), 3) / 1e12
+    return {"hbm_read_gbps": round(hbm, 1), "mfma_bf16_tflops": round(mfma, 1)}
+
+
 def knee_bench(args) -> None:
-    """Append-prefill sweep (one layer, 64 query heads, 8 KV heads, head_dim
-    128): attention time per launch for each prefix P and row count R, the
-    knee where more rows stop being nearly free, and the largest draft length
-    k whose hybrid step (k + (k+1)k rows) fits under it."""
+    """Free-token-slot knee and the draft length it gives.
+
+    The knee is where an append-prefill attention layer (64 query heads, 8 KV
+    heads, head_dim 128) turns from HBM-bound to MFMA-bound: the roofline
+    crossing at this box's measured HBM read rate and MFMA rate
+    (draft_length.roofline_knee). The measured latency sweep over prefixes P
+    and row counts R (32 rotated caches per timed graph) is reported beside
+    it with its hinge fit t = c + max(a, b R) (draft_length.hinge_fit). The
+    draft length for the Qwen3-8B step (4 query heads per KV head) is the
+    largest k whose packed rows fit under the knee at P = 4096."""
     import math
 
     import torch
 
     import ar_self_speculative_amd as tidar
+    from ar_self_speculative_amd import draft_length as dl
 
     Hq, Hkv, D = 64, 8, 128
     Ps, Rs = (512, 1024, 2048, 4096), (1, 8, 16, 32, 64, 128, 256, 512)
+    ceil = knee_ceilings()
     gen = torch.Generator(device="cuda").manual_seed(0)
     nbuf = 32  # distinct caches per timed graph (32 x 16.8 MB at P=4096 > the 256 MB last-level cache)
     table = {}
@@ -432,28 +471,29 @@ def knee_bench(args) -> None:
             run()
             g = _capture(run)
             table[(P, R)] = _time_graph(g, 3) * 1e3 / nbuf
-    knee = {}
+        del kcs, vcs
+    g_sweep, g_step = Hq // Hkv, SHAPE["num_q_heads"] // SHAPE["num_kv_heads"]
+    knees, fits = {}, {}
     for P in Ps:
-        base = table[(P, 1)]
-        knee[P] = max(R for R in Rs if table[(P, R)] <= 1.25 * base)
-    g = Hq // Hkv
-    # packed query rows (rows x group) at the knee; the Qwen3-8B decode step
-    # packs k + (k+1)k rows x 4 query heads per KV head
-    packed = knee[4096] * g
-    g_step = SHAPE["num_q_heads"] // SHAPE["num_kv_heads"]
-    k_pick = max([k for k in (1, 2, 4, 8, 16) if (k + (k + 1) * k) * g_step <= packed] or [1])
+        knees[P] = dl.roofline_knee(prefix=P, q_heads=Hq, kv_heads=Hkv, head_dim=D, hbm_gbps=ceil["hbm_read_gbps"],
+                                    mfma_tflops=ceil["mfma_bf16_tflops"])
+        f = dl.hinge_fit(Rs, [table[(P, R)] for R in Rs])
+        fits[P] = {key: round(v, 3) for key, v in f.items()}
+    k_pick = dl.draft_length(knees[4096], sweep_group=g_sweep, step_group=g_step)
     print(json.dumps({
-        "metric": "append-prefill attention us per launch (64 q heads, 8 kv heads, d 128) and its knee",
+        "metric": "free-token-slot knee (append-prefill attention, 64 q heads, 8 kv heads, d 128) and draft length",
         "unit": "us", "n_gpus": 1, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "one layer, batch 1, append-prefill sweep", "P": list(Ps), "R": list(Rs),
                    "caches_rotated": nbuf},
+        "ceilings": ceil,
         "us": {str(P): [round(table[(P, R)], 2) for R in Rs] for P in Ps},
-        "knee_rule": "largest R with time <= 1.25 x time at R = 1",
-        "knee_R": {str(P): knee[P] for P in Ps},
-        "knee_rows_times_group": {str(P): knee[P] * g for P in Ps},
-        "draft_length_at_P4096": {"rule": "largest k whose step packs at most the knee's rows x group",
-                                  "k": k_pick, "rows": k_pick + (k_pick + 1) * k_pick,
-                                  "packed_rows": (k_pick + (k_pick + 1) * k_pick) * g_step},
+        "knee_rule": "rows where MFMA time equals HBM time at the measured ceilings (roofline crossing)",
+        "knee_rows": {str(P): round(knees[P], 2) for P in Ps},
+        "sweep_hinge_fit": {str(P): fits[P] for P in Ps},
+        "draft_length_at_P4096": {"rule": "largest k in (1, 2, 4, 8, 16) whose step's rows x 4 query heads per kv "
+                                          "head fit under the knee's rows x 8",
+                                  "k": k_pick, "rows": dl.step_rows(k_pick),
+                                  "packed_rows": dl.step_rows(k_pick) * g_step},
     }), flush=True)
 
 
@@ -468,8 +508,19 @@ def loop_bench(args) -> None:
     from ar_self_speculative_amd.loop import TiDARLoop, TinyDecoder
 
     s = SHAPE
-    L, Hq, Hkv, D, P, V, k = s["layers"], s["num_q_heads"], s["num_kv_heads"], s["head_dim"], s["P"], s["vocab"], \
-        s["k"]
+    L, Hq, Hkv, D, P, V = s["layers"], s["num_q_heads"], s["num_kv_heads"], s["head_dim"], s["P"], s["vocab"]
+    k_rule = None
+    if args.k == "auto":
+        # the draft length from the free-slot knee at this box's measured ceilings
+        from ar_self_speculative_amd import draft_length as dl
+
+        ceil = knee_ceilings()
+        knee = dl.roofline_knee(prefix=P, q_heads=Hq, kv_heads=Hkv, head_dim=D, hbm_gbps=ceil["hbm_read_gbps"],
+                                mfma_tflops=ceil["mfma_bf16_tflops"])
+        k = dl.draft_length(knee, sweep_group=Hq // Hkv, step_group=Hq // Hkv)
+        k_rule = {"ceilings": ceil, "knee_rows": round(knee, 2), "k": k}
+    else:
+        k = int(args.k) if args.k else s["k"]
     model = TinyDecoder(vocab=V, hidden=4096, layers=L, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, mlp=12288,
                         seed=0)
     cap = P + 2048
@@ -515,12 +566,13 @@ def loop_bench(args) -> None:
         print(f"device status flags set: {int(lp.status.item())}", file=sys.stderr)
         sys.exit(1)
     print(json.dumps({
-        "metric": "TiDAR step loop NFE/s with a random-weight Qwen3-8B-shape decoder (k=16 region rows, P~4096)",
+        "metric": f"TiDAR step loop NFE/s with a random-weight Qwen3-8B-shape decoder (k={k} region rows, P~4096)",
         "value": round(1e3 / ms, 2), "unit": "NFE/s", "n_gpus": 1, "steps": reps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "dtype": "bf16", "data": "synthetic, random weights",
-        "config": {"workload": "qwen3-8b-shape decoder (hidden 4096, 36 layers, 32/8 heads, head_dim 128, "
-                               "MLP 12288, vocab 151936), batch 1, prefix 4096, k=16 region rows (288 rows)",
+        "config": {"workload": f"qwen3-8b-shape decoder (hidden 4096, 36 layers, 32/8 heads, head_dim 128, "
+                               f"MLP 12288, vocab 151936), batch 1, prefix 4096, k={k} region rows ({lp.R} rows)",
                    "layers": L, "prefix": P, "k": k, "rows": lp.R},
+        "draft_length_rule": k_rule,
         "tokens_per_nfe": round(tokens_per_nfe, 3),
         "attention_ms_per_step": round(ms_attn, 4),
         "attention_share": round(ms_attn / ms, 4),
@@ -540,6 +592,9 @@ def main():
                     help="only time likelihood mode: one causal forward scoring R tokens (P=4096), and exit")
     ap.add_argument("--loop", action="store_true",
                     help="only time the TiDAR step loop with a random-weight Qwen3-8B-shaped decoder, and exit")
+    ap.add_argument("--k", default="", metavar="K|auto",
+                    help="draft length of --loop (default 16); 'auto' takes it from the free-slot knee at this "
+                         "box's measured HBM and MFMA ceilings")
     ap.add_argument("--config5", action="store_true",
                     help="only time the ragged batch (8 sequences, k=8, 36 layers, 64 chained steps) and exit")
     ap.add_argument("--ceilings", action="store_true",
