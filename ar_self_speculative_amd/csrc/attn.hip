@@ -214,7 +214,10 @@ __device__ __forceinline__ void lds_barrier() {
 // rescale of the accumulators on almost every tile.
 constexpr float kSlack = 8.f;
 
-template <int D, int NQT>
+// LSE32: accumulate the row sum in fp32 from the unrounded probabilities
+// (used when the caller asks for the log-sum-exp); otherwise from the
+// bf16-rounded ones that also feed P V, with one packed dot per pair.
+template <int D, int NQT, bool LSE32 = false>
 struct Wave {
   static constexpr int DSTEPS = D / 16;
   static constexpr int DT = D / 32;
@@ -333,7 +336,10 @@ struct Wave {
       const float p1 = __builtin_amdgcn_exp2f(fmaf(s[nt][(i + 1) >> 4][(i + 1) & 15], sl2, -muse));
       const f32x2 pp = {p0, p1};
       const bf16x2 h = __builtin_convertvector(pp, bf16x2);
-      l[nt] = __builtin_amdgcn_fdot2_f32_bf16(h, one, l[nt], false);
+      if (LSE32)
+        l[nt] += p0 + p1;
+      else
+        l[nt] = __builtin_amdgcn_fdot2_f32_bf16(h, one, l[nt], false);
       pb[nt][i >> 3][i & 7] = h[0];
       pb[nt][i >> 3][(i & 7) + 1] = h[1];
     }
@@ -479,11 +485,12 @@ struct TileSeq {
 // Iteration t of the tile loop when tile t+1 is a full prefix tile: the
 // fully interleaved step with no other path, so the accumulators keep their
 // registers across iterations.
-template <int D, int NQT, int WAVES>
-__device__ __forceinline__ void main_iter(Wave<D, NQT>& st, lds_u8* __restrict__ kb_dst,
+template <int D, int NQT, int WAVES, bool LSE32>
+__device__ __forceinline__ void main_iter(Wave<D, NQT, LSE32>& st, lds_u8* __restrict__ kb_dst,
                                           const lds_u8* __restrict__ kb_next, const lds_u8* __restrict__ vb_cur,
                                           lds_u8* __restrict__ vb_dst, const TileSeq& seq, int t, int wave,
-                                          float sl2, typename Wave<D, NQT>::S& sA, typename Wave<D, NQT>::S& sB) {
+                                          float sl2, typename Wave<D, NQT, LSE32>::S& sA,
+                                          typename Wave<D, NQT, LSE32>::S& sB) {
   if (t + 2 < seq.count()) {
     const TileSrc a = seq.at(t + 2);
     copy_tile<D, WAVES>(make_rsrc(a.k, a.bytes), a.vo, a.row0, a.row_bytes, kb_dst, wave);
@@ -505,12 +512,12 @@ __device__ __forceinline__ void main_iter(Wave<D, NQT>& st, lds_u8* __restrict__
 // copies in flight. The next tile's scores are masked between the step's
 // phases when it needs it (the partial last prefix tile, or step keys under
 // the region rule); the loop's last tile (P V only) is peeled by the caller.
-template <int D, int NQT, int WAVES>
-__device__ __forceinline__ void tile_iter(Wave<D, NQT>& st, lds_u8* __restrict__ kb_dst,
+template <int D, int NQT, int WAVES, bool LSE32>
+__device__ __forceinline__ void tile_iter(Wave<D, NQT, LSE32>& st, lds_u8* __restrict__ kb_dst,
                                           const lds_u8* __restrict__ kb_next, const lds_u8* __restrict__ vb_cur,
                                           lds_u8* __restrict__ vb_dst, const TileSeq& seq, int t, int wave, int lane,
-                                          const RowRule (&rules)[NQT], float sl2, typename Wave<D, NQT>::S& sA,
-                                          typename Wave<D, NQT>::S& sB) {
+                                          const RowRule (&rules)[NQT], float sl2,
+                                          typename Wave<D, NQT, LSE32>::S& sA, typename Wave<D, NQT, LSE32>::S& sB) {
   // t + 1 < count(): the next tile exists (the caller peels the last tile)
   if (t + 2 < seq.count()) {
     const TileSrc a = seq.at(t + 2);
@@ -536,11 +543,11 @@ __device__ __forceinline__ void tile_iter(Wave<D, NQT>& st, lds_u8* __restrict__
 // to a dword (each below 2^16, checked on the host): a_qt_s = qtiles | S << 16,
 // a_hkv_g = Hkv | g << 16, a_k_bl = k | block_len << 16; a_nwg is the grid size.
 
-template <int D, int NQT, int WAVES>
+template <int D, int NQT, int WAVES, bool LSE32>
 __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kernel(
     const int32_t* __restrict__ a_len, const void* __restrict__ a_q, const void* __restrict__ a_kc, uint32_t a_qt_s,
     uint32_t a_hkv_g, uint32_t a_k_bl, int a_R, int a_nwg, int a_cap, int a_chunk, int a_max_len, AttnParams p) {
-  using W = Wave<D, NQT>;
+  using W = Wave<D, NQT, LSE32>;
   using L = Lay<D>;
   constexpr int DSTEPS = D / 16, DT = D / 32;
   constexpr int WROWS = 32 * NQT;      // query rows per wave
@@ -703,13 +710,13 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
     // all reads of K[t] (QK^T of tile t) and V[t-1] (PV of tile t-1) are
     // done before this iteration's copies overwrite their buffers
     __syncthreads();
-    main_iter<D, NQT, WAVES>(st, par ? KB[1] : KB[0], par ? KB[0] : KB[1], par ? VB[1] : VB[0],
+    main_iter<D, NQT, WAVES, LSE32>(st, par ? KB[1] : KB[0], par ? KB[0] : KB[1], par ? VB[1] : VB[0],
                              par ? VB[0] : VB[1], seq, t, wave, sl2, sA, sB);
   }
   for (; t + 1 < ntot; ++t) {
     const int par = t & 1;
     __syncthreads();
-    tile_iter<D, NQT, WAVES>(st, par ? KB[1] : KB[0], par ? KB[0] : KB[1], par ? VB[1] : VB[0],
+    tile_iter<D, NQT, WAVES, LSE32>(st, par ? KB[1] : KB[0], par ? KB[0] : KB[1], par ? VB[1] : VB[0],
                              par ? VB[0] : VB[1], seq, t, wave, lane, rules, sl2, sA, sB);
   }
   if (t < ntot) {  // the last tile: P V only (its V is in VB[t & 1])
@@ -1471,15 +1478,21 @@ hipError_t launch_attn_bf16(const AttnParams& p, hipStream_t stream) {
   const uint32_t k_bl = (uint32_t)p.k | ((uint32_t)p.block_len << 16);
 #define TIDAR_ATTN_ARGS                                                                                       \
   p.cache_len, p.q, p.k_cache, qt_s, hkv_g, k_bl, p.R, (int)grid, p.cap, p.chunk, p.max_len, p
-  // 128 query rows per workgroup (four waves of 32 rows), or 256 (eight waves, head_dim 128)
-  if (p.D == 128 && p.waves == 8)
-    hipLaunchKernelGGL((attn_bf16_kernel<128, 1, 8>), dim3((unsigned)grid), dim3(512), 0, stream, TIDAR_ATTN_ARGS);
-  else if (p.D == 128 && p.waves == 4)
-    hipLaunchKernelGGL((attn_bf16_kernel<128, 1, 4>), dim3((unsigned)grid), dim3(256), 0, stream, TIDAR_ATTN_ARGS);
-  else if (p.D == 64 && p.waves == 4)
-    hipLaunchKernelGGL((attn_bf16_kernel<64, 1, 4>), dim3((unsigned)grid), dim3(256), 0, stream, TIDAR_ATTN_ARGS);
-  else
+  // 128 query rows per workgroup (four waves of 32 rows), or 256 (eight
+  // waves, head_dim 128); the row sums in fp32 when the caller wants the LSE
+  const bool l32 = p.lse != nullptr;
+#define TIDAR_LAUNCH(D_, W_, L_) \
+  hipLaunchKernelGGL((attn_bf16_kernel<D_, 1, W_, L_>), dim3((unsigned)grid), dim3(64 * W_), 0, stream, TIDAR_ATTN_ARGS)
+  if (p.D == 128 && p.waves == 8) {
+    if (l32) TIDAR_LAUNCH(128, 8, true); else TIDAR_LAUNCH(128, 8, false);
+  } else if (p.D == 128 && p.waves == 4) {
+    if (l32) TIDAR_LAUNCH(128, 4, true); else TIDAR_LAUNCH(128, 4, false);
+  } else if (p.D == 64 && p.waves == 4) {
+    if (l32) TIDAR_LAUNCH(64, 4, true); else TIDAR_LAUNCH(64, 4, false);
+  } else {
     return hipErrorInvalidValue;
+  }
+#undef TIDAR_LAUNCH
 #undef TIDAR_ATTN_ARGS
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.S == 1) return e;

@@ -29,7 +29,7 @@ def attn_desc(case, num_splits=0, max_cache_len=None):
         num_splits=num_splits)
 
 
-def run_attn(case, layer=0, num_splits=0, cache_len=None, max_cache_len=None, with_status=False):
+def run_attn(case, layer=0, num_splits=0, cache_len=None, max_cache_len=None, with_status=False, with_lse=True):
     desc = attn_desc(case, num_splits, max_cache_len)
     q = dev_array(case, "q", layer)
     ks = dev_array(case, "k_step", layer)
@@ -42,9 +42,9 @@ def run_attn(case, layer=0, num_splits=0, cache_len=None, max_cache_len=None, wi
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
     wsb = tidar.attn_workspace_bytes(desc)
     ws = torch.zeros(max(wsb, 256), dtype=torch.uint8, device="cuda") if wsb else None
-    tidar.attn_step(desc, q, ks, vs, kc, vc, lens, out, lse, status, ws)
+    tidar.attn_step(desc, q, ks, vs, kc, vc, lens, out, lse if with_lse else None, status, ws)
     torch.cuda.synchronize()
-    res = (out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64))
+    res = (out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64) if with_lse else None)
     if with_status:
         return res + (int(status.item()),)
     return res

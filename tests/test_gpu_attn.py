@@ -1,10 +1,10 @@
 """GPU parity of tidar_attn_step against the fp64 oracle.
 
 Tolerances: max-abs 1e-5 for fp32 inputs and 2e-2 for bf16 inputs, on the
-stored output. LSE: 1e-5 for fp32; for bf16 the row sum is accumulated from
-the bf16-rounded probabilities that also feed the P.V product, each within a
-relative 2^-8 (half a bf16 ulp) of its exact value, so the log of the sum
-is within 2^-8.
+stored output. LSE: 1e-5 for fp32 and 1e-4 for bf16 (when the LSE is asked
+for, the bf16 kernel sums each row's probabilities in fp32 before they are
+rounded for the P.V product; without it the sum is taken over the rounded
+values, which the full-layer test below exercises on the output).
 """
 import numpy as np
 import pytest
@@ -17,7 +17,7 @@ from tests.gpu_util import run_attn, oracle_inputs
 pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-5, "bf16": 2e-2}
-LSE_TOL = {"f32": 1e-5, "bf16": 2.0 ** -8}
+LSE_TOL = {"f32": 1e-5, "bf16": 1e-4}
 
 
 def _oracle_full(case, layer=0, cache_len=None):
@@ -137,6 +137,17 @@ def test_config3_full_depth_sampled():
     print(f"[parity] cfg3 36 layers sampled: max-abs {worst:.3e}", flush=True)
     assert worst <= TOL["bf16"]
     del rng
+
+
+def test_config3_one_layer_every_element_at_the_bench_launch():
+    """One full Qwen3-8B-shaped layer (P = 4096, k = 16, 288 rows x 32 query
+    heads) compared with the oracle at every output element, launched exactly
+    as the bench times it: the library's split plan, no LSE requested."""
+    c = config_attn(3, seed=2, layers=1)
+    out, _ = run_attn(c, with_lse=False)
+    ref, _ = _oracle_full(c)
+    assert np.isfinite(out).all()
+    assert _report("cfg3 one layer, every element, bench launch", out, ref, TOL["bf16"]) <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
