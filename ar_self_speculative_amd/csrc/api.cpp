@@ -145,9 +145,9 @@ int reject_common(int32_t batch, int32_t k, int32_t vocab, const float* ar_logit
   const size_t bsz = ((size_t)2 * batch * p.nchunks * sizeof(double) + 255) / 256 * 256;
   p.row_stats = reinterpret_cast<float2*>(ws);
   p.resid_sums = reinterpret_cast<double*>(ws + a);
-  p.decision = reinterpret_cast<int32_t*>(ws + a + bsz);
-  const size_t dsz = ((size_t)batch * 2 * sizeof(int32_t) + 255) / 256 * 256;
-  p.row_mz = reinterpret_cast<float2*>(ws + a + bsz + dsz);
+  p.arrive = reinterpret_cast<int32_t*>(ws + a + bsz);
+  const size_t dsz = ((size_t)batch * sizeof(int32_t) + 255) / 256 * 256;
+  p.gathered = reinterpret_cast<float*>(ws + a + bsz + dsz);
   hipError_t e = tidar::launch_reject(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "reject launch");
   return TIDAR_OK;

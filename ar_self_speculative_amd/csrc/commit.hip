@@ -13,14 +13,40 @@
 namespace tidar {
 namespace {
 
-__global__ __launch_bounds__(256) void kv_commit_kernel(CommitParams p) {
+// Each workgroup loads the first kCommitThreads 16-byte pieces of its
+// (layer, sequence, KV head)'s k candidate draft rows together with the
+// accept length, and stores those among the first n rows: the row loads need
+// not wait for the accept length (one memory round trip instead of two).
+// Pieces past n are read and dropped; pieces past the first kCommitThreads
+// (k * head_dim * elem_bytes > kCommitThreads * 16) are copied once n is known.
+constexpr int kCommitThreads = 256;
+
+__global__ __launch_bounds__(kCommitThreads) void kv_commit_kernel(CommitParams p) {
   int idx = blockIdx.x;
   const int h = idx % p.Hkv;
   idx /= p.Hkv;
   const int b = idx % p.B;
   const int l = idx / p.B;
 
-  int n = p.accept_len[b];
+  const size_t row_bytes = (size_t)p.D * p.elem_bytes;
+  const int cpr = (int)(row_bytes / 16);  // 16-byte chunks per row
+  const size_t src0 = ((((size_t)l * p.B + b) * p.step_rows) * p.Hkv + h) * row_bytes;
+  const size_t src_row_stride = (size_t)p.Hkv * row_bytes;
+  const char* ks = reinterpret_cast<const char*>(p.k_step);
+  const char* vs = reinterpret_cast<const char*>(p.v_step);
+  char* kc = reinterpret_cast<char*>(p.k_cache);
+  char* vc = reinterpret_cast<char*>(p.v_cache);
+  // this thread's candidate piece first: its address does not depend on the accept length
+  const int c = threadIdx.x;
+  const int total = p.k * cpr;
+  uint4 kr = make_uint4(0, 0, 0, 0), vr = make_uint4(0, 0, 0, 0);
+  if (c < total) {
+    const size_t so = src0 + (size_t)(c / cpr) * src_row_stride + (size_t)(c % cpr) * 16;
+    kr = *reinterpret_cast<const uint4*>(ks + so);
+    vr = *reinterpret_cast<const uint4*>(vs + so);
+  }
+
+  const int n = p.accept_len[b];
   const int start = p.len_in[b];
   bool ok = true;
   if (n < 0 || n > p.k) {
@@ -33,17 +59,15 @@ __global__ __launch_bounds__(256) void kv_commit_kernel(CommitParams p) {
   if (l == 0 && h == 0 && threadIdx.x == 0) p.len_out[b] = ok ? start + n : start;
   if (!ok) return;
 
-  const size_t row_bytes = (size_t)p.D * p.elem_bytes;
-  const int cpr = (int)(row_bytes / 16);  // 16-byte chunks per row
-  const size_t src0 = ((((size_t)l * p.B + b) * p.step_rows) * p.Hkv + h) * row_bytes;
-  const size_t src_row_stride = (size_t)p.Hkv * row_bytes;
   const size_t dst0 = ((((size_t)l * p.B + b) * p.Hkv + h) * p.cap + start) * row_bytes;
-  const char* ks = reinterpret_cast<const char*>(p.k_step);
-  const char* vs = reinterpret_cast<const char*>(p.v_step);
-  char* kc = reinterpret_cast<char*>(p.k_cache);
-  char* vc = reinterpret_cast<char*>(p.v_cache);
-  for (int c = threadIdx.x; c < n * cpr; c += blockDim.x) {
-    const int i = c / cpr, q = c % cpr;
+  const int keep = n * cpr;
+  if (c < keep) {
+    const size_t d0 = dst0 + (size_t)(c / cpr) * row_bytes + (size_t)(c % cpr) * 16;
+    *reinterpret_cast<uint4*>(kc + d0) = kr;
+    *reinterpret_cast<uint4*>(vc + d0) = vr;
+  }
+  for (int cc = kCommitThreads + threadIdx.x; cc < keep; cc += kCommitThreads) {
+    const int i = cc / cpr, q = cc % cpr;
     const size_t so = src0 + i * src_row_stride + (size_t)q * 16;
     const size_t d0 = dst0 + (size_t)i * row_bytes + (size_t)q * 16;
     *reinterpret_cast<uint4*>(kc + d0) = *reinterpret_cast<const uint4*>(ks + so);
@@ -55,7 +79,7 @@ __global__ __launch_bounds__(256) void kv_commit_kernel(CommitParams p) {
 
 hipError_t launch_kv_commit(const CommitParams& p, hipStream_t stream) {
   const unsigned grid = (unsigned)((size_t)p.L * p.B * p.Hkv);
-  hipLaunchKernelGGL(kv_commit_kernel, dim3(grid), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(kv_commit_kernel, dim3(grid), dim3(kCommitThreads), 0, stream, p);
   return hipGetLastError();
 }
 

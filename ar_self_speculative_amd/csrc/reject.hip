@@ -5,16 +5,18 @@
 // first rejection draw from normalised max(0, p_i - q_i), after k acceptances
 // draw a bonus token from p_k).
 //
-// Three HBM-streaming launches, all with a fixed reduction order so results
+// Two HBM-streaming launches, all with a fixed reduction order so results
 // are run-to-run deterministic:
 //   1. rej_stats : per (row, vocab chunk) max and sum of exp over the 2k+1
-//                  logit rows of each sequence (one read of all logits);
-//   2. rej_resid : every workgroup of a sequence merges the row statistics,
+//                  logit rows of each sequence (one read of all logits),
+//                  and the drafts' own logits, stored by the threads that
+//                  hold them;
+//   2. rej_draw  : every workgroup of a sequence merges the row statistics,
 //                  evaluates the acceptance chain from the gathered p_i(d),
 //                  q_i(d) (identical in all of them) and sums the residual
 //                  (or bonus) weights of its vocab chunk, and p_n alone for
-//                  the rounding fallback, in fp64;
-//   3. rej_pick  : per sequence, locates the chunk whose running mass passes
+//                  the rounding fallback, in fp64; the last of them to
+//                  finish locates the chunk whose running mass passes
 //                  u * total, then the token inside it (inverse CDF in token
 //                  id order).
 // Trust mixing (TiDAR review, 设计取舍: trust AR vs trust diffusion logits,
@@ -100,27 +102,6 @@ __device__ __forceinline__ const float* row_ptr(const RejectParams& p, int b, in
                    : p.diff + ((size_t)b * p.k + (rr - p.k - 1)) * p.V;
 }
 
-// Load this thread's kPer elements of a chunk (scaled by 1/T); -inf past the end.
-__device__ __forceinline__ void load_chunk(const float* x, int e0, int e1, float inv_t, bool vec4,
-                                           float (&v)[kPer]) {
-  if (vec4 && e0 + kChunk <= e1) {
-#pragma unroll
-    for (int j = 0; j < kPer / 4; ++j) {
-      const float4 f = *reinterpret_cast<const float4*>(x + e0 + 4 * (threadIdx.x + kThreads * j));
-      v[4 * j + 0] = f.x * inv_t;
-      v[4 * j + 1] = f.y * inv_t;
-      v[4 * j + 2] = f.z * inv_t;
-      v[4 * j + 3] = f.w * inv_t;
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int idx = e0 + threadIdx.x + kThreads * j;
-      v[j] = idx < e1 ? x[idx] * inv_t : kNegInf;
-    }
-  }
-}
-
 // The three sampler kernels take the fields their first loads need as
 // leading scalar arguments, which the dispatch preloads into scalar registers
 // (this file is built with kernel-argument preloading): the logit, draft and
@@ -130,47 +111,166 @@ __device__ __forceinline__ const float* row_ptr_a(const float* ar, const float* 
   return rr <= k ? ar + ((size_t)b * (k + 1) + rr) * V : diff + ((size_t)b * k + (rr - k - 1)) * V;
 }
 
-__global__ __launch_bounds__(kThreads) void rej_stats_kernel(const float* __restrict__ a_ar,
-                                                             const float* __restrict__ a_diff, int a_V,
-                                                             uint32_t a_k_nch, int a_mix, float a_inv_t, float a_lam,
-                                                             float a_mu, RejectParams p) {
-  __shared__ float red[4];
-  const int k = (int)(a_k_nch & 0xffff), nch = (int)(a_k_nch >> 16);
-  const int c = blockIdx.x % nch;
-  const int row = blockIdx.x / nch;
-  const int nrows = 2 * k + 1;
-  const int b = row / nrows, rr = row % nrows;
-  const bool target = rr < k;  // a verification target (not the bonus row)
-  const float* x = row_ptr_a(a_ar, a_diff, k, a_V, b, target && a_mix == 2 ? k + 1 + rr : rr);
-  const int e0 = c * kChunk, e1 = min(e0 + kChunk, a_V);
-  const bool vec4 = (a_V & 3) == 0;
-  float v[kPer];
-  if (target && a_mix == 1) {
-    // mixed target: (lam * a + mu * d) / T, formed exactly as in the draws
-    float w[kPer];
-    load_chunk(x, e0, e1, 1.f, vec4, v);
-    load_chunk(row_ptr_a(a_ar, a_diff, k, a_V, b, k + 1 + rr), e0, e1, 1.f, vec4, w);
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) v[j] = fmaf(a_lam, v[j], a_mu * w[j]) * a_inv_t;
+// Element `off` of a chunk (0 <= off < chunk length): the thread that holds
+// it after load_chunk, and its index in that thread's kPer values.
+__device__ __forceinline__ void chunk_owner(int off, bool vec, int& thread, int& slot) {
+  if (vec) {
+    const int j = off / (4 * kThreads), rem = off % (4 * kThreads);
+    thread = rem / 4;
+    slot = 4 * j + rem % 4;
   } else {
-    load_chunk(x, e0, e1, a_inv_t, vec4, v);
+    thread = off % kThreads;
+    slot = off / kThreads;
   }
-  float mx = kNegInf;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) mx = fmaxf(mx, v[j]);
-  mx = block_max(mx, red);
-  float s = 0.f;
-  if (mx != kNegInf) {
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) s += expf(v[j] - mx);
-  }
-  s = block_sumf(s, red);
-  if (threadIdx.x == 0) p.row_stats[((size_t)b * nrows + rr) * nch + c] = make_float2(mx, s);
 }
 
-// The mixed logit of a verification target (mix == 1), as rej_stats forms it.
-__device__ __forceinline__ float mix_logit(const RejectParams& p, float a, float d) {
-  return fmaf(p.lam, a, p.mu * d);
+// Statistics pass: each workgroup takes kPPW consecutive (row, chunk) pairs
+// of one sequence and issues all their loads in straight-line code before
+// any arithmetic (past-the-end elements load a valid address and are masked
+// to -inf), so one memory round trip covers all of them. One pair per
+// workgroup measured fastest (two or four per workgroup leave some CUs with
+// twice the bytes of others at the Qwen3 vocabulary). Per pair: the
+// maximum and the sum of exponentials of the temperature-scaled logits. The
+// thread that holds a draft's token in a pair also stores that logit
+// (scaled; the mixed one for a mixed target), so the accept chain needs no
+// gather of its own. Workgroup 0 of each sequence clears that sequence's
+// arrival counter for the draw pass that follows in stream order.
+//
+// MIX: how the targets of rows 0..k-1 are formed (0 AR, 1 mixed, 2
+// diffusion); VEC: the vocabulary is a multiple of 4, so each thread loads
+// float4s (element 4 * (thread + kThreads * j) + e of a chunk), else single
+// floats (element thread + kThreads * j).
+constexpr int kPPW = 1;
+
+template <bool VEC>
+__device__ __forceinline__ void load_chunk_masked(const float* x, int e0, int e1, float (&v)[kPer]) {
+  if (VEC) {
+#pragma unroll
+    for (int j = 0; j < kPer / 4; ++j) {
+      const int idx = e0 + 4 * ((int)threadIdx.x + kThreads * j);
+      const float4 f = *reinterpret_cast<const float4*>(x + (idx < e1 ? idx : 0));
+      v[4 * j + 0] = f.x;
+      v[4 * j + 1] = f.y;
+      v[4 * j + 2] = f.z;
+      v[4 * j + 3] = f.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int idx = e0 + (int)threadIdx.x + kThreads * j;
+      v[j] = x[idx < e1 ? idx : 0];
+    }
+  }
+}
+
+template <bool VEC>
+__device__ __forceinline__ bool chunk_elem_valid(int e0, int e1, int j) {
+  return VEC ? e0 + 4 * ((int)threadIdx.x + kThreads * (j / 4)) < e1 : e0 + (int)threadIdx.x + kThreads * j < e1;
+}
+
+template <int MIX, bool VEC>
+__global__ __launch_bounds__(kThreads) void rej_stats_kernel(const float* __restrict__ a_ar,
+                                                             const float* __restrict__ a_diff, int a_V,
+                                                             uint32_t a_k_nch, float a_inv_t, float a_lam, float a_mu,
+                                                             RejectParams p) {
+  __shared__ float red[kThreads / 64][kPPW];
+  const int k = (int)(a_k_nch & 0xffff), nch = (int)(a_k_nch >> 16);
+  const int nrows = 2 * k + 1, npairs = nrows * nch;
+  const int G = (npairs + kPPW - 1) / kPPW;
+  const int b = blockIdx.x / G, g0 = (blockIdx.x % G) * kPPW;
+  float v[kPPW][kPer];
+  float w[MIX == 1 ? kPPW : 1][kPer];
+#pragma unroll
+  for (int pp = 0; pp < kPPW; ++pp) {
+    const int pair = min(g0 + pp, npairs - 1);  // a short last group repeats its last pair (not stored)
+    const int rr = pair / nch, c = pair % nch;
+    const bool target = rr < k;  // a verification target (not the bonus row)
+    const int e0 = c * kChunk, e1 = min(e0 + kChunk, a_V);
+    load_chunk_masked<VEC>(row_ptr_a(a_ar, a_diff, k, a_V, b, MIX == 2 && target ? k + 1 + rr : rr), e0, e1, v[pp]);
+    // mixed target: the diffusion row of the same position (other rows load their own row again)
+    if (MIX == 1)
+      load_chunk_masked<VEC>(row_ptr_a(a_ar, a_diff, k, a_V, b, target ? k + 1 + rr : rr), e0, e1, w[pp]);
+  }
+  // keep the arithmetic below the loads: the scheduler would otherwise start
+  // scaling the first values as they arrive, stalling the loads behind them
+  __builtin_amdgcn_sched_barrier(0);
+  // the draft proposed on each pair's row (-1: the bonus row, or past the end)
+  int dsel[kPPW];
+#pragma unroll
+  for (int pp = 0; pp < kPPW; ++pp) {
+    const int pair = g0 + pp, rr = pair / nch;
+    dsel[pp] = (pair < npairs && rr != k) ? p.drafts[(size_t)b * k + (rr < k ? rr : rr - k - 1)] : -1;
+  }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // scale (and mix) in the same order as the draws, mask past-the-end elements,
+  // then the block maxima of the kPPW pairs (waves combined in a fixed order)
+#pragma unroll
+  for (int pp = 0; pp < kPPW; ++pp) {
+    const int pair = min(g0 + pp, npairs - 1);
+    const int c = pair % nch;
+    const bool mixed = MIX == 1 && pair / nch < k;
+    const int e0 = c * kChunk, e1 = min(e0 + kChunk, a_V);
+    float m = kNegInf;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      float x = v[pp][j];
+      if (MIX == 1) x = mixed ? fmaf(a_lam, x, a_mu * w[pp][j]) : x;
+      x *= a_inv_t;
+      v[pp][j] = chunk_elem_valid<VEC>(e0, e1, j) ? x : kNegInf;
+      m = fmaxf(m, v[pp][j]);
+    }
+    m = wave_max(m);
+    if (lane == 0) red[wave][pp] = m;
+  }
+  __syncthreads();
+  float mx[kPPW];
+#pragma unroll
+  for (int pp = 0; pp < kPPW; ++pp) mx[pp] = fmaxf(fmaxf(red[0][pp], red[1][pp]), fmaxf(red[2][pp], red[3][pp]));
+  // the drafts' logits, by the threads that hold them
+#pragma unroll
+  for (int pp = 0; pp < kPPW; ++pp) {
+    const int pair = g0 + pp, rr = pair / nch, c = pair % nch;
+    const int d = dsel[pp];
+    const int e0 = c * kChunk, e1 = min(e0 + kChunk, a_V);
+    if (d >= e0 && d < e1) {
+      int t, slot;
+      chunk_owner(d - e0, VEC, t, slot);
+      if ((int)threadIdx.x == t) {
+        float val = 0.f;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) val = j == slot ? v[pp][j] : val;
+        const int i = rr < k ? rr : rr - k - 1;
+        p.gathered[(size_t)b * 2 * k + (rr < k ? i : k + i)] = val;
+      }
+    }
+  }
+  if (g0 == 0 && threadIdx.x == 0) p.arrive[b] = 0;
+  float sm[kPPW];
+#pragma unroll
+  for (int pp = 0; pp < kPPW; ++pp) {
+    float s = 0.f;
+    if (mx[pp] != kNegInf) {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) s += expf(v[pp][j] - mx[pp]);
+    }
+    sm[pp] = wave_sumf(s);
+  }
+  __syncthreads();  // every wave has read the maxima
+#pragma unroll
+  for (int pp = 0; pp < kPPW; ++pp)
+    if (lane == 0) red[wave][pp] = sm[pp];
+  __syncthreads();
+  if (threadIdx.x < kPPW && g0 + (int)threadIdx.x < npairs) {
+    const int pp = threadIdx.x, pair = g0 + pp;
+    float m = kNegInf, s = 0.f;
+#pragma unroll
+    for (int q = 0; q < kPPW; ++q)
+      if (q == pp) {
+        m = mx[q];
+        s = ((red[0][q] + red[1][q]) + red[2][q]) + red[3][q];
+      }
+    p.row_stats[((size_t)b * nrows + pair / nch) * nch + pair % nch] = make_float2(m, s);
+  }
 }
 
 // Weight of token t for the final draw: residual max(0, p_n - q_n) after a
@@ -187,7 +287,8 @@ struct DrawRows {
   float s;         // log2(e) / T
   float ba, ra;    // m_target * log2(e), 1 / z_target
   float bq, rq;
-  __device__ __forceinline__ void init(const RejectParams& p, int b, int n, const float2* mz) {
+  // sa, sq: merged (max, sum exp) of the target row n and of its diffusion row
+  __device__ __forceinline__ void init(const RejectParams& p, int b, int n, float2 sa, float2 sq) {
     const float l2e = 1.4426950408889634f;
     const int k = p.k;
     a = row_ptr(p, b, n);
@@ -197,7 +298,6 @@ struct DrawRows {
     lam = p.lam;
     mu = p.mu;
     s = p.inv_temp * l2e;
-    const float2 sa = mz[n], sq = n < k ? mz[k + 1 + n] : make_float2(0.f, 1.f);
     ba = sa.x * l2e;
     ra = 1.f / sa.y;
     bq = q ? sq.x * l2e : 0.f;
@@ -265,150 +365,30 @@ __device__ __forceinline__ double block_scan_incl(double x, double* red, double*
   return x + off;
 }
 
-__global__ __launch_bounds__(kThreads) void rej_resid_kernel(const int32_t* __restrict__ a_drafts,
-                                                             const float* __restrict__ a_uni,
-                                                             const float2* __restrict__ a_stats, uint32_t a_k_nch,
-                                                             RejectParams p) {
-  __shared__ float2 mz[2 * kMaxK + 1];
-  __shared__ float2 st_lds[kStage];
-  __shared__ float rho[kMaxK];
-  __shared__ float uni[kMaxK];
-  __shared__ int n_sh;
-  __shared__ double redd[4];
-  const int k = (int)(a_k_nch & 0xffff), nch = (int)(a_k_nch >> 16);
-  const int c = blockIdx.x % nch, b = blockIdx.x / nch;
-  const int nrows = 2 * k + 1;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  // the draft tokens' logits are gathered first so their latency overlaps
-  // the statistics merge
-  const int i = threadIdx.x;
-  int d = -1;
-  float da = 0.f, dq = 0.f;  // logits of draft i under its target and diffusion rows
-  if (i < k) {
-    d = a_drafts[(size_t)b * k + i];
-    uni[i] = a_uni[(size_t)b * (k + 1) + i];
-    if (d >= 0 && d < p.V) {
-      dq = row_ptr(p, b, k + 1 + i)[d];
-      da = p.mix == 2 ? dq : row_ptr(p, b, i)[d];
-      if (p.mix == 1) da = mix_logit(p, da, dq);  // the target's logit at the draft
-    }
-  }
-  // per-row statistics: stage every (row, chunk) pair of this sequence in
-  // LDS with one round of loads, then merge each row across one wave
-  const int total = nrows * nch;
-  if (total <= kStage) {
-    const float2* g = a_stats + (size_t)b * total;
-    float2 v[kStage / kThreads];
-#pragma unroll
-    for (int j = 0; j < kStage / kThreads; ++j) {
-      const int t = threadIdx.x + kThreads * j;
-      if (t < total) v[j] = g[t];
-    }
-#pragma unroll
-    for (int j = 0; j < kStage / kThreads; ++j) {
-      const int t = threadIdx.x + kThreads * j;
-      if (t < total) st_lds[t] = v[j];
-    }
-    __syncthreads();
-  }
-  // each row merged by a group of kGroup lanes (all rows at once when the
-  // statistics fit in LDS), else by one wave per row from global memory
-  const bool staged = total <= kStage;
-  const int nr_pass = staged ? kThreads / kGroup : kThreads / 64;
-  for (int rr0 = 0; rr0 < nrows; rr0 += nr_pass) {
-    const int rr = rr0 + (staged ? (int)threadIdx.x / kGroup : wave);
-    const float2 v = staged ? merge_row_group(st_lds, p.nchunks, rr, nrows, threadIdx.x % kGroup)
-                            : (rr < nrows ? merge_row_wave(p, b, rr, lane) : make_float2(0.f, 0.f));
-    if (rr < nrows && (staged ? threadIdx.x % kGroup == 0 : lane == 0)) {
-      mz[rr] = v;
-      if (c == 0) p.row_mz[(size_t)b * nrows + rr] = v;
-      if (!(isfinite(v.x) && v.y > 0.f && isfinite(v.y)) && c == 0 && p.dev_status) atomicOr(p.dev_status, 8);
-    }
-  }
-  __syncthreads();
-  if (i < k) {
-    float r = 0.f;
-    if (d < 0 || d >= p.V) {
-      if (c == 0 && p.dev_status) atomicOr(p.dev_status, 16);
-    } else {
-      const float2 sa = mz[i], sq = mz[k + 1 + i];
-      const float pa = expf(da * p.inv_temp - sa.x) / sa.y;
-      const float pq = expf(dq * p.inv_temp - sq.x) / sq.y;
-      r = pq > 0.f ? pa / pq : INFINITY;
-    }
-    rho[i] = r;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int n = 0;
-    while (n < k && uni[n] < fminf(1.f, rho[n])) ++n;
-    n_sh = n;
-  }
-  __syncthreads();
-  const int n = n_sh;
-  if (c == 0) {
-    for (int i = threadIdx.x; i < k; i += kThreads)
-      if (p.ratio) p.ratio[(size_t)b * k + i] = rho[i];
-    if (threadIdx.x == 0) {
-      p.accept_len[b] = n;
-      p.decision[2 * b] = n;
-      p.decision[2 * b + 1] = 0;
-    }
-  }
-  DrawRows dr;
-  dr.init(p, b, n, mz);
-  // per chunk: mass of the draw distribution, and of p_n alone (the
-  // fallback when the residual vanishes through rounding)
-  const int e0 = c * kChunk, e1 = min(e0 + kChunk, p.V);
-  float xa[kPer], xq[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int t = min(e0 + threadIdx.x + kThreads * j, e1 - 1);
-    xa[j] = dr.needs_a() ? dr.a[t] : 0.f;
-    xq[j] = dr.q ? dr.q[t] : 0.f;
-  }
-  double acc = 0.0, acc_a = 0.0;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    if (e0 + (int)threadIdx.x + kThreads * j < e1) {
-      const float pt = dr.pt(dr.target(xa[j], xq[j]));
-      const float w = dr.sub ? fmaxf(0.f, pt - dr.pq(xq[j])) : pt;
-      acc += (double)w;
-      acc_a += (double)pt;
-    }
-  }
-  acc = block_sumd(acc, redd);
-  acc_a = block_sumd(acc_a, redd);
-  if (threadIdx.x == 0) {
-    p.resid_sums[(size_t)b * p.nchunks + c] = acc;
-    p.resid_sums[((size_t)p.B + b) * p.nchunks + c] = acc_a;
-  }
-}
-
-__global__ __launch_bounds__(kThreads) void rej_pick_kernel(const int32_t* __restrict__ a_decision,
-                                                            const double* __restrict__ a_sums, uint32_t a_k_nch,
-                                                            int a_B, RejectParams p) {
+// Token pick for sequence b, run by the last draw-pass workgroup of the
+// sequence once every chunk's masses are visible: inverse CDF in token-id
+// order, first over the chunk masses, then inside the chosen chunk.
+__device__ __forceinline__ void pick_token(const RejectParams& p, int b, int k, int nch, DrawRows dr) {
   __shared__ double red[4];
   __shared__ double sums[kMaxChunks];
   __shared__ int pick_c, last_c, first_t, last_t;
   __shared__ double pick_base;
-  const int k = (int)(a_k_nch & 0xffff), nch = (int)(a_k_nch >> 16);
-  const int b = blockIdx.x, nrows = 2 * k + 1;
   // thread t owns chunks [cpt*t, cpt*t + cpt)
   const int cpt = (nch + kThreads - 1) / kThreads;
   const int c0 = cpt * threadIdx.x, c1 = min(c0 + cpt, nch);
+  double* a_sums = p.resid_sums;
   double mine = 0.0;
-  for (int c = c0; c < c1; ++c) mine += (sums[c] = a_sums[(size_t)b * nch + c]);
-  const int n = a_decision[2 * b];
-  DrawRows dr;
-  dr.init(p, b, n, p.row_mz + (size_t)b * nrows);
+  for (int c = c0; c < c1; ++c)
+    mine += (sums[c] = __hip_atomic_load(a_sums + (size_t)b * nch + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   double total;
   double incl = block_scan_incl(mine, red, &total);
   if (!(total > 0.0)) {
     // the residual vanished through rounding: draw from p_n instead
     dr.sub = false;
     mine = 0.0;
-    for (int c = c0; c < c1; ++c) mine += (sums[c] = a_sums[((size_t)a_B + b) * nch + c]);
+    for (int c = c0; c < c1; ++c)
+      mine += (sums[c] = __hip_atomic_load(a_sums + ((size_t)p.B + b) * nch + c, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT));
     incl = block_scan_incl(mine, red, &total);
   }
   const double target = (double)p.uniforms[(size_t)b * (k + 1) + k] * total;
@@ -439,19 +419,34 @@ __global__ __launch_bounds__(kThreads) void rej_pick_kernel(const int32_t* __res
   }
   __syncthreads();
   const int cp = pick_c != 0x7fffffff ? pick_c : max(last_c, 0);
-  if (threadIdx.x == 0) {
-    double base = 0.0;
-    for (int c = 0; c < cp; ++c) base += sums[c];
+  // mass before the chosen chunk, summed by its owner in the order of the search above
+  if (c0 <= cp && cp < c1) {
+    double base = incl - mine;
+    for (int c = c0; c < cp; ++c) base += sums[c];
     pick_base = base;
   }
   // inverse CDF inside the chosen chunk: thread t owns kPer consecutive tokens
+  // (rows loaded unconditionally, as in the draw pass)
   const int e0 = cp * kChunk, e1 = min(e0 + kChunk, p.V);
+  const int t0 = e0 + (int)threadIdx.x * kPer;
+  const float* qrow = dr.q ? dr.q : dr.a;
   float w[kPer], xq[kPer];
+  if ((p.V & 3) == 0) {
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int t = min(e0 + (int)threadIdx.x * kPer + j, e1 - 1);
-    w[j] = dr.needs_a() ? dr.a[t] : 0.f;
-    xq[j] = dr.q ? dr.q[t] : 0.f;
+    for (int j = 0; j < kPer / 4; ++j) {
+      const int off = t0 + 4 * j < e1 ? t0 + 4 * j : e0;
+      const float4 fa = *reinterpret_cast<const float4*>(dr.a + off);
+      const float4 fq = *reinterpret_cast<const float4*>(qrow + off);
+      w[4 * j] = fa.x, w[4 * j + 1] = fa.y, w[4 * j + 2] = fa.z, w[4 * j + 3] = fa.w;
+      xq[4 * j] = fq.x, xq[4 * j + 1] = fq.y, xq[4 * j + 2] = fq.z, xq[4 * j + 3] = fq.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int t = min(t0 + j, e1 - 1);
+      w[j] = dr.a[t];
+      xq[j] = qrow[t];
+    }
   }
   double tsum = 0.0;
 #pragma unroll
@@ -483,11 +478,141 @@ __global__ __launch_bounds__(kThreads) void rej_pick_kernel(const int32_t* __res
   if (threadIdx.x == 0) p.next_token[b] = first_t != 0x7fffffff ? first_t : max(last_t, 0);
 }
 
+__global__ __launch_bounds__(kThreads) void rej_draw_kernel(const int32_t* __restrict__ a_drafts,
+                                                             const float* __restrict__ a_uni,
+                                                             const float2* __restrict__ a_stats, uint32_t a_k_nch,
+                                                             RejectParams p) {
+  __shared__ float2 mz[2 * kMaxK + 1];
+  __shared__ float2 st_lds[kStage];
+  __shared__ float rho[kMaxK];
+  __shared__ float uni[kMaxK];
+  __shared__ int n_sh, last_sh;
+  __shared__ double redd[4];
+  const int k = (int)(a_k_nch & 0xffff), nch = (int)(a_k_nch >> 16);
+  const int c = blockIdx.x % nch, b = blockIdx.x / nch;
+  const int nrows = 2 * k + 1;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // the drafts, their scaled logits under the target and diffusion rows
+  // (stored by the statistics pass) and the uniforms: independent loads that
+  // go out together with the statistics below
+  const int i = threadIdx.x;
+  int d = -1;
+  float da = 0.f, dq = 0.f;
+  if (i < k) {
+    d = a_drafts[(size_t)b * k + i];
+    uni[i] = a_uni[(size_t)b * (k + 1) + i];
+    da = p.gathered[(size_t)b * 2 * k + i];
+    dq = p.gathered[(size_t)b * 2 * k + k + i];
+  }
+  // per-row statistics: stage every (row, chunk) pair of this sequence in
+  // LDS with one round of loads, then merge each row across one wave
+  const int total = nrows * nch;
+  if (total <= kStage) {
+    const float2* g = a_stats + (size_t)b * total;
+    float2 v[kStage / kThreads];
+#pragma unroll
+    for (int j = 0; j < kStage / kThreads; ++j) {
+      const int t = threadIdx.x + kThreads * j;
+      if (t < total) v[j] = g[t];
+    }
+#pragma unroll
+    for (int j = 0; j < kStage / kThreads; ++j) {
+      const int t = threadIdx.x + kThreads * j;
+      if (t < total) st_lds[t] = v[j];
+    }
+    __syncthreads();
+  }
+  // each row merged by a group of kGroup lanes (all rows at once when the
+  // statistics fit in LDS), else by one wave per row from global memory
+  const bool staged = total <= kStage;
+  const int nr_pass = staged ? kThreads / kGroup : kThreads / 64;
+  for (int rr0 = 0; rr0 < nrows; rr0 += nr_pass) {
+    const int rr = rr0 + (staged ? (int)threadIdx.x / kGroup : wave);
+    const float2 v = staged ? merge_row_group(st_lds, p.nchunks, rr, nrows, threadIdx.x % kGroup)
+                            : (rr < nrows ? merge_row_wave(p, b, rr, lane) : make_float2(0.f, 0.f));
+    if (rr < nrows && (staged ? threadIdx.x % kGroup == 0 : lane == 0)) {
+      mz[rr] = v;
+      if (!(isfinite(v.x) && v.y > 0.f && isfinite(v.y)) && c == 0 && p.dev_status) atomicOr(p.dev_status, 8);
+    }
+  }
+  __syncthreads();
+  if (i < k) {
+    float r = 0.f;
+    if (d < 0 || d >= p.V) {
+      if (c == 0 && p.dev_status) atomicOr(p.dev_status, 16);
+    } else {
+      const float2 sa = mz[i], sq = mz[k + 1 + i];
+      const float pa = expf(da - sa.x) / sa.y;
+      const float pq = expf(dq - sq.x) / sq.y;
+      r = pq > 0.f ? pa / pq : INFINITY;
+    }
+    rho[i] = r;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int n = 0;
+    while (n < k && uni[n] < fminf(1.f, rho[n])) ++n;
+    n_sh = n;
+  }
+  __syncthreads();
+  const int n = n_sh;
+  if (c == 0) {
+    for (int i = threadIdx.x; i < k; i += kThreads)
+      if (p.ratio) p.ratio[(size_t)b * k + i] = rho[i];
+    if (threadIdx.x == 0) p.accept_len[b] = n;
+  }
+  DrawRows dr;
+  dr.init(p, b, n, mz[n], n < k ? mz[k + 1 + n] : make_float2(0.f, 1.f));
+  // per chunk: mass of the draw distribution, and of p_n alone (the
+  // fallback when the residual vanishes through rounding)
+  const int e0 = c * kChunk, e1 = min(e0 + kChunk, p.V);
+  // both rows loaded unconditionally (the bonus draw has no diffusion row and
+  // reads its AR row twice; a diffusion target reads the unused AR row)
+  const float* qrow = dr.q ? dr.q : dr.a;
+  float xa[kPer], xq[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int t = min(e0 + (int)threadIdx.x + kThreads * j, e1 - 1);
+    xa[j] = dr.a[t];
+    xq[j] = qrow[t];
+  }
+  double acc = 0.0, acc_a = 0.0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    if (e0 + (int)threadIdx.x + kThreads * j < e1) {
+      const float pt = dr.pt(dr.target(xa[j], xq[j]));
+      const float w = dr.sub ? fmaxf(0.f, pt - dr.pq(xq[j])) : pt;
+      acc += (double)w;
+      acc_a += (double)pt;
+    }
+  }
+  acc = block_sumd(acc, redd);
+  acc_a = block_sumd(acc_a, redd);
+  // Publish this chunk's masses; the last of the sequence's workgroups to
+  // arrive sees all of them and draws the token. The masses are stored at
+  // device scope (written through this XCD's L2), and the arrival count goes
+  // out once those stores are complete: no release fence, which would write
+  // back the XCD's whole L2 in every workgroup. Only the drawing workgroup
+  // acquires, and it reads the masses with device-scope loads.
+  if (threadIdx.x == 0) {
+    __hip_atomic_store(p.resid_sums + (size_t)b * nch + c, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(p.resid_sums + ((size_t)p.B + b) * nch + c, acc_a, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): both stores are complete
+    const int prev = __hip_atomic_fetch_add(p.arrive + b, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_sh = prev == nch - 1;
+  }
+  __syncthreads();
+  if (!last_sh) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  pick_token(p, b, k, nch, dr);
+}
+
 }  // namespace
 
 // Scratch of the allocation-free entry point: the sampler's workspace (per
-// (row, chunk) statistics, per-chunk draw masses, the decision, merged row
-// statistics) lives in this file-scope device array instead of a caller
+// (row, chunk) statistics, per-chunk draw masses, arrival counters, the
+// drafts' gathered logits) lives in this file-scope device array instead of a caller
 // buffer. Each GPU holds its own copy for the life of the process. Host code
 // never passes the array's name to a kernel (on the host it is only a
 // stand-in); it passes the device address hipGetSymbolAddress returns,
@@ -530,10 +655,10 @@ hipError_t reject_scratch(int device, void** out) {
 size_t reject_workspace_bytes(int B, int k, int V) {
   const size_t nchunks = ((size_t)V + kChunk - 1) / kChunk;
   size_t bytes = 0;
-  bytes += ((size_t)B * (2 * k + 1) * nchunks * sizeof(float2) + 255) / 256 * 256;
-  bytes += ((size_t)2 * B * nchunks * sizeof(double) + 255) / 256 * 256;
-  bytes += ((size_t)B * 2 * sizeof(int32_t) + 255) / 256 * 256;
-  bytes += ((size_t)B * (2 * k + 1) * sizeof(float2) + 255) / 256 * 256;
+  bytes += ((size_t)B * (2 * k + 1) * nchunks * sizeof(float2) + 255) / 256 * 256;  // row_stats
+  bytes += ((size_t)2 * B * nchunks * sizeof(double) + 255) / 256 * 256;            // resid_sums
+  bytes += ((size_t)B * sizeof(int32_t) + 255) / 256 * 256;                          // arrive
+  bytes += ((size_t)B * 2 * k * sizeof(float) + 255) / 256 * 256;                    // gathered
   return bytes;
 }
 
@@ -546,17 +671,25 @@ int reject_max_k() { return kMaxK; }
 int reject_max_chunks() { return kMaxChunks; }
 
 hipError_t launch_reject(const RejectParams& p, hipStream_t stream) {
-  const unsigned stats_grid = (unsigned)((size_t)p.nchunks * p.B * (2 * p.k + 1));
+  const unsigned stats_grid =
+      (unsigned)((size_t)p.B * (((size_t)(2 * p.k + 1) * p.nchunks + kPPW - 1) / kPPW));
   const uint32_t k_nch = (uint32_t)p.k | ((uint32_t)p.nchunks << 16);
-  hipLaunchKernelGGL(rej_stats_kernel, dim3(stats_grid), dim3(kThreads), 0, stream, p.ar, p.diff, p.V, k_nch, p.mix,
-                     p.inv_temp, p.lam, p.mu, p);
+  const bool vec = (p.V & 3) == 0;
+#define TIDAR_STATS(MIX, VEC)                                                                                    \
+  hipLaunchKernelGGL((rej_stats_kernel<MIX, VEC>), dim3(stats_grid), dim3(kThreads), 0, stream, p.ar, p.diff, p.V, \
+                     k_nch, p.inv_temp, p.lam, p.mu, p)
+  if (p.mix == 1) {
+    if (vec) TIDAR_STATS(1, true); else TIDAR_STATS(1, false);
+  } else if (p.mix == 2) {
+    if (vec) TIDAR_STATS(2, true); else TIDAR_STATS(2, false);
+  } else {
+    if (vec) TIDAR_STATS(0, true); else TIDAR_STATS(0, false);
+  }
+#undef TIDAR_STATS
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(rej_resid_kernel, dim3((unsigned)((size_t)p.nchunks * p.B)), dim3(kThreads), 0, stream, p.drafts,
+  hipLaunchKernelGGL(rej_draw_kernel, dim3((unsigned)((size_t)p.nchunks * p.B)), dim3(kThreads), 0, stream, p.drafts,
                      p.uniforms, p.row_stats, k_nch, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(rej_pick_kernel, dim3(p.B), dim3(kThreads), 0, stream, p.decision, p.resid_sums, k_nch, p.B, p);
   return hipGetLastError();
 }
 

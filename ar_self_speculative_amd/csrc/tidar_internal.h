@@ -88,8 +88,10 @@ struct RejectParams {
   int32_t* dev_status;
   float2* row_stats;    // [B, 2k+1, nchunks] (max, sum exp) per chunk
   double* resid_sums;   // [2, B, nchunks] mass per chunk of the draw distribution, then of p_n alone
-  int32_t* decision;    // [B, 2]: accept length, source row kind
-  float2* row_mz;       // [B, 2k+1] merged (max, sum exp) of every row
+  int32_t* arrive;      // [B] draw-pass workgroups of the sequence that have published their chunk
+                        // masses (cleared by the statistics pass)
+  float* gathered;      // [B, 2k]: the drafts' scaled logits under their target rows, then their
+                        // diffusion rows
 };
 size_t reject_workspace_bytes(int B, int k, int V);
 // Size of the device-resident scratch behind tidar_reject_sample_noalloc, and
