@@ -39,6 +39,13 @@ long sat_mul(long a, long b) {
   return __builtin_mul_overflow(a, b, &r) ? LONG_MAX : r;
 }
 
+// 64-key tiles of step keys a query tile may see: the whole causal run in
+// append-prefill mode, else the drafts plus one block
+int local_tiles_of(const tidar_attn_desc* d) {
+  const long R = (long)d->k + (long)d->num_blocks * (d->num_blocks > 0 ? d->block_len : 0);
+  return d->num_blocks == 0 ? (int)((R + 63) / 64) : (d->k + 63) / 64 + (d->block_len + 63) / 64;
+}
+
 int check_desc(const tidar_attn_desc* d, tidar::AttnPlan* plan) {
   if (!d) return fail(TIDAR_E_INVALID, "desc is NULL");
   if (d->dtype != TIDAR_DTYPE_F32 && d->dtype != TIDAR_DTYPE_BF16)
@@ -73,10 +80,7 @@ int check_desc(const tidar_attn_desc* d, tidar::AttnPlan* plan) {
   const long qe = sat_mul(sat_mul(sat_mul(d->batch, R), d->num_q_heads), D);
   const long ce = sat_mul(sat_mul(sat_mul(d->batch, d->num_kv_heads), d->cache_capacity), D);
   if (qe > kMaxElems || ce > kMaxElems) return fail(TIDAR_E_UNSUPPORTED, "tensor too large for 32-bit indexing");
-  // 64-key tiles of step keys a query tile may see: the whole causal run in
-  // append-prefill mode, else the drafts plus one block
-  const int local_tiles = d->num_blocks == 0 ? (int)((R + 63) / 64)
-                                             : (d->k + 63) / 64 + (d->block_len + 63) / 64;
+  const int local_tiles = local_tiles_of(d);
   if (d->dtype == TIDAR_DTYPE_BF16 && (d->num_kv_heads > 0xffff || d->num_q_heads / d->num_kv_heads > 0xffff ||
                                         d->k > 0xffff || (d->num_blocks > 0 && d->block_len > 0xffff)))
     return fail(TIDAR_E_UNSUPPORTED, "bf16 path: KV heads, group size, k and block_len must be below 65536");
@@ -226,14 +230,17 @@ int tidar_attn_step(const tidar_attn_desc* desc, const void* q, const void* k_st
   p.waves = plan.waves;
   p.decode = plan.decode;
   p.fused_merge = plan.fused_merge;
+  p.ragged = plan.ragged;
+  p.local_tiles = local_tiles_of(desc);
   p.sm_scale = desc->sm_scale;
   p.scale_log2 = desc->sm_scale * 1.4426950408889634f;
   if (plan.S > 1 || plan.decode) {
-    // [arrival counters (decode path)] [split outputs] [split log-sum-exps]
-    const size_t rows = (size_t)plan.S * p.B * p.R * p.Hq;
+    // [arrival counters (decode path) or split table (ragged)] [split outputs] [split log-sum-exps]
+    const size_t rows = (size_t)plan.S * (plan.ragged ? 1 : p.B) * p.R * p.Hq;
     const size_t elem = desc->dtype == TIDAR_DTYPE_BF16 ? 2 : 4;
     char* ws = static_cast<char*>(workspace);
     p.counters = reinterpret_cast<int32_t*>(ws);
+    p.split_tab = plan.ragged ? reinterpret_cast<int32_t*>(ws) : nullptr;
     p.part_o = ws + plan.counter_bytes;
     const size_t o_bytes = (rows * p.D * elem + 255) / 256 * 256;
     p.part_lse = reinterpret_cast<float*>(ws + plan.counter_bytes + o_bytes);

@@ -169,6 +169,19 @@ struct Lay {
   static constexpr int NLD = 2 * NCP;            // 1 KB copies per tile
 };
 
+// Copy i (0 <= i < NLD / WAVES) of this wave's share of a tile copy (the
+// scalar offset is wave-uniform by construction; readfirstlane tells the
+// compiler so).
+template <int D, int WAVES>
+__device__ __forceinline__ void copy_one(__amdgpu_buffer_rsrc_t r, uint32_t vo, int row0, uint32_t row_bytes,
+                                         lds_u8* dst, int wave, int i) {
+  const int j = wave + WAVES * i;
+  const int cp = j >> 1, h = j & 1;
+  const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)(row0 + 32 * h) * row_bytes + 32u * cp);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + cp * kCPS + h * 1024),
+                                           16, vo, so, 0, 0);
+}
+
 // Global -> LDS copy of one 64-key tile (rows row0 .. row0+63 of a buffer
 // resource whose rows are row_bytes apart), without passing through
 // registers. Copy j moves column pair j/2 of keys 32*(j%2) .. +31; lane l
@@ -178,14 +191,7 @@ template <int D, int WAVES>
 __device__ __forceinline__ void copy_tile(__amdgpu_buffer_rsrc_t r, uint32_t vo, int row0, uint32_t row_bytes,
                                           lds_u8* dst, int wave) {
 #pragma unroll
-  for (int i = 0; i < Lay<D>::NLD / WAVES; ++i) {
-    const int j = wave + WAVES * i;
-    const int cp = j >> 1, h = j & 1;
-    // the scalar offset is wave-uniform by construction; readfirstlane tells the compiler so
-    const uint32_t so = __builtin_amdgcn_readfirstlane((uint32_t)(row0 + 32 * h) * row_bytes + 32u * cp);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(dst + cp * kCPS + h * 1024),
-                                             16, vo, so, 0, 0);
-  }
+  for (int i = 0; i < Lay<D>::NLD / WAVES; ++i) copy_one<D, WAVES>(r, vo, row0, row_bytes, dst, wave, i);
 }
 
 // Lane l of a copy lands on LDS slot half (l%2) of key l/2; it fetches the
@@ -484,24 +490,23 @@ struct TileSeq {
 
 // Iteration t of the tile loop when tile t+1 is a full prefix tile: the
 // fully interleaved step with no other path, so the accumulators keep their
-// registers across iterations.
+// registers across iterations. The scores of tile t are in s_cur, those of
+// tile t+1 land in s_next (the caller alternates the two). All of the
+// iteration's copies go out first: issued one at a time from inside the
+// step instead, they stalled the waves that issued them there and the CU's
+// throughput did not rise.
 template <int D, int NQT, int WAVES, bool LSE32>
 __device__ __forceinline__ void main_iter(Wave<D, NQT, LSE32>& st, lds_u8* __restrict__ kb_dst,
                                           const lds_u8* __restrict__ kb_next, const lds_u8* __restrict__ vb_cur,
                                           lds_u8* __restrict__ vb_dst, const TileSeq& seq, int t, int wave,
-                                          float sl2, typename Wave<D, NQT, LSE32>::S& sA,
-                                          typename Wave<D, NQT, LSE32>::S& sB) {
+                                          float sl2, const typename Wave<D, NQT, LSE32>::S& s_cur,
+                                          typename Wave<D, NQT, LSE32>::S& s_next) {
   if (t + 2 < seq.count()) {
     const TileSrc a = seq.at(t + 2);
     copy_tile<D, WAVES>(make_rsrc(a.k, a.bytes), a.vo, a.row0, a.row_bytes, kb_dst, wave);
   }
   copy_tile<D, WAVES>(make_rsrc(seq.pv, seq.pbytes), seq.pvo, (t + 1) * kBN, seq.prb, vb_dst, wave);
-  st.template step<true, true>(kb_next, vb_cur, sA, sB, sl2);
-#pragma unroll
-  for (int nt = 0; nt < NQT; ++nt) {
-    sA[nt][0] = sB[nt][0];
-    sA[nt][1] = sB[nt][1];
-  }
+  st.template step<true, true>(kb_next, vb_cur, s_cur, s_next, sl2);
   wait_copies();
 }
 
@@ -573,20 +578,74 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
   int w = remap_xcd((int)__builtin_amdgcn_workgroup_id_x(), a_nwg);
   const int qt = w % qtiles;
   w /= qtiles;
-  const int s = w % S;
-  w /= S;
-  const int kvh = w % Hkv;
-  const int b = w / Hkv;
+  int s, kvh, b, Sb, chunk, len = 0;
+  size_t prow_off;  // partial rows of this split: [prow_off, prow_off + rows) of part_o / part_lse, in output rows
+  if (p.ragged) {
+    // The sequence and split of slot `slot`: every workgroup shares the S
+    // slots out the same way from the clamped lengths. Sequence i weighs
+    // w_i = its prefix tiles plus the step-key tiles of its last split; with
+    // c = ceil(sum w / (S - B)) it takes S_i = ceil(w_i / c) >= 1 slots
+    // (sum S_i <= S), and its splits cover ceil(tiles_i / S_i) tiles each.
+    const int slot = w % S;
+    kvh = w / S;
+    const int B = p.B, lt = p.local_tiles;
+    int wsum = 0;
+    for (int i = 0; i < B; ++i) {
+      const int li = min(max(a_len[i], 0), a_max_len);
+      wsum += (li + kBN - 1) / kBN + lt;
+    }
+    const int E = S - B;  // > 0 by the plan
+    const int c = (wsum + E - 1) / E;
+    const bool writer = qt == 0 && kvh == 0 && slot == 0 && tid == 0;
+    int start = 0, bstart = 0;
+    b = -1;
+    Sb = 1;
+    for (int i = 0; i < B; ++i) {
+      const int li = min(max(a_len[i], 0), a_max_len);
+      const int si = max(1, ((li + kBN - 1) / kBN + lt + c - 1) / c);
+      if (writer) {
+        p.split_tab[2 * i] = start;
+        p.split_tab[2 * i + 1] = si;
+      }
+      if (b < 0 && slot < start + si) {
+        b = i;
+        bstart = start;
+        Sb = si;
+      }
+      start += si;
+    }
+    b = __builtin_amdgcn_readfirstlane(b);
+    if (b < 0) return;  // a slot no sequence needed
+    s = __builtin_amdgcn_readfirstlane(slot - bstart);
+    Sb = __builtin_amdgcn_readfirstlane(Sb);
+    const int raw = a_len[b];
+    if (raw < 0 || raw > a_max_len) {
+      if (tid == 0 && p.dev_status) atomicOr(p.dev_status, 1);
+    }
+    len = __builtin_amdgcn_readfirstlane(min(max(raw, 0), a_max_len));
+    chunk = __builtin_amdgcn_readfirstlane(((len + kBN - 1) / kBN + Sb - 1) / Sb * kBN);
+    prow_off = (size_t)(bstart + s - b) * a_R * Hkv * g;
+  } else {
+    s = w % S;
+    w /= S;
+    kvh = w % Hkv;
+    b = w / Hkv;
+    Sb = S;
+    chunk = a_chunk;
+    prow_off = (size_t)s * p.B * a_R * Hkv * g;
+  }
 
   // The first prefix tile's K rows do not depend on the cache length: their
   // copy goes out first, bounded by the host's max_len instead (rows below
   // max_len lie inside the cache). Rows at or past the length that it brings
   // in are masked to -inf before any use; V rows past the length are never
   // loaded (their copies are bounded by the length), so P V sees only zeros
-  // there.
-  const bool last = (s == S - 1);
-  const int kbeg = s * a_chunk;
-  const int nk_hint = __builtin_amdgcn_readfirstlane(max(0, (last ? a_max_len : min(kbeg + a_chunk, a_max_len)) - kbeg));
+  // there. (Ragged batches already know the length: no early copy.)
+  const bool last = (s == Sb - 1);
+  const int kbeg = s * chunk;
+  const int nk_hint = p.ragged ? 0
+                               : __builtin_amdgcn_readfirstlane(
+                                     max(0, (last ? a_max_len : min(kbeg + chunk, a_max_len)) - kbeg));
   const size_t head_off = (size_t)(b * Hkv + kvh) * a_cap * D + (size_t)kbeg * D;
   const uint32_t pvo = copy_voff(lane, D * 2);
   if (nk_hint > 0)
@@ -620,13 +679,37 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
     st.l[nt] = 0.f;
   }
 
-  int len = __builtin_amdgcn_readfirstlane(a_len[b]);  // uniform: keeps the tile loop scalar
-  if (len < 0 || len > a_max_len) {
-    if (tid == 0 && p.dev_status) atomicOr(p.dev_status, 1);
-    len = min(max(len, 0), a_max_len);
+  if (!p.ragged) {
+    len = __builtin_amdgcn_readfirstlane(a_len[b]);  // uniform: keeps the tile loop scalar
+    if (len < 0 || len > a_max_len) {
+      if (tid == 0 && p.dev_status) atomicOr(p.dev_status, 1);
+      len = min(max(len, 0), a_max_len);
+    }
   }
-  const int kend = last ? len : min(kbeg + a_chunk, len);
+  const int kend = last ? len : min(kbeg + chunk, len);
   const int nk = max(0, kend - kbeg);
+
+  // A split that lies wholly past its sequence's length (ragged batches)
+  // has no keys: it records an empty partial (log-sum-exp -inf, which the
+  // merge weighs by exactly zero without reading the partial) and leaves,
+  // skipping the prologue's waits and the epilogue's 32 KB partial store.
+  // Its early K copy may still be in flight, so it waits for that first.
+  if (!last && nk == 0) {
+    wait_copies();
+    if (half == 0) {
+      const __amdgpu_buffer_rsrc_t lrsrc = make_rsrc(p.part_lse + prow_off, 0xFFFFFFFFu);
+#pragma unroll
+      for (int nt = 0; nt < NQT; ++nt) {
+        const int m = qt * BM + wave * WROWS + 32 * nt + l32;
+        if (m < M) {
+          const int r = m / g;
+          const uint32_t orow = (uint32_t)((b * a_R + r) * Hq + kvh * g + (m - r * g));
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(kNegInf), lrsrc, (int)(orow * 4u), 0, kStoreDevice);
+        }
+      }
+    }
+    return;
+  }
 
   const float sl2 = p.scale_log2;
 
@@ -704,14 +787,26 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
   if (ntot == 0) wait_copies();  // the early copy lands before KB[0] is reused for staging
   // iterations whose next tile is a full prefix tile run a loop of their own
   const int tmain = __builtin_amdgcn_readfirstlane(max(0, min(nk / kBN, ntot) - 1));
+  // Unrolled by two: the scores of the current tile alternate between sA
+  // and sB, so no register copies are needed between iterations. Each
+  // barrier: all reads of K[t] (QK^T of tile t) and V[t-1] (PV of tile t-1)
+  // are done before this iteration's copies overwrite their buffers.
   int t = 0;
-  for (; t < tmain; ++t) {
-    const int par = t & 1;
-    // all reads of K[t] (QK^T of tile t) and V[t-1] (PV of tile t-1) are
-    // done before this iteration's copies overwrite their buffers
+  for (; t + 1 < tmain; t += 2) {
     __syncthreads();
-    main_iter<D, NQT, WAVES, LSE32>(st, par ? KB[1] : KB[0], par ? KB[0] : KB[1], par ? VB[1] : VB[0],
-                             par ? VB[0] : VB[1], seq, t, wave, sl2, sA, sB);
+    main_iter<D, NQT, WAVES, LSE32>(st, KB[0], KB[1], VB[0], VB[1], seq, t, wave, sl2, sA, sB);
+    __syncthreads();
+    main_iter<D, NQT, WAVES, LSE32>(st, KB[1], KB[0], VB[1], VB[0], seq, t + 1, wave, sl2, sB, sA);
+  }
+  if (t < tmain) {  // an odd count: one more (t even), then the scores move back to sA
+    __syncthreads();
+    main_iter<D, NQT, WAVES, LSE32>(st, KB[0], KB[1], VB[0], VB[1], seq, t, wave, sl2, sA, sB);
+#pragma unroll
+    for (int nt = 0; nt < NQT; ++nt) {
+      sA[nt][0] = sB[nt][0];
+      sA[nt][1] = sB[nt][1];
+    }
+    ++t;
   }
   for (; t + 1 < ntot; ++t) {
     const int par = t & 1;
@@ -758,8 +853,8 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
       } else {
         // log2-domain log-sum-exp of this split's partial, written through like the partial
         const float e = ltot > 0.f ? st.m[nt] + log2f(ltot) : kNegInf;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(e), make_rsrc(p.part_lse + (size_t)s * p.B * a_R * Hq,
-                                              0xFFFFFFFFu), (int)(orow * 4u), 0, kStoreDevice);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(e), make_rsrc(p.part_lse + prow_off, 0xFFFFFFFFu),
+                                              (int)(orow * 4u), 0, kStoreDevice);
       }
     }
 #pragma unroll
@@ -782,8 +877,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
     // merge may start; written through, that traffic drains while other
     // workgroups still compute. Offsets stay below 2^32: the output holds
     // fewer than 2^31 elements of 2 bytes (checked on the host).
-    u16* const obase = S == 1 ? reinterpret_cast<u16*>(p.out)
-                              : reinterpret_cast<u16*>(p.part_o) + (size_t)s * p.B * a_R * Hq * D;
+    u16* const obase = S == 1 ? reinterpret_cast<u16*>(p.out) : reinterpret_cast<u16*>(p.part_o) + prow_off * D;
     const __amdgpu_buffer_rsrc_t orsrc = make_rsrc(obase, 0xFFFFFFFFu);
 #pragma unroll
     for (int j = 0; j < PASSES; ++j) {
@@ -1259,10 +1353,14 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p) {
 template <bool BF16>
 // Arguments are plain scalars so that they are preloaded into scalar registers
 // at dispatch and the partial loads need not wait for the argument block.
+// Split partials of an output row: with tab (ragged batches), sequence b's
+// splits sit in partial blocks tab[2b] .. tab[2b] + tab[2b+1] - 1 of
+// seq_rows rows each; without, split s of every row is block s of `rows`.
 __global__ __launch_bounds__(256) void attn_merge_kernel(const void* __restrict__ part_o,
                                                         const float* __restrict__ part_lse, void* __restrict__ out,
                                                         float* __restrict__ lse, uint32_t rows, uint32_t D,
-                                                        uint32_t S) {
+                                                        uint32_t S, const int32_t* __restrict__ tab,
+                                                        uint32_t seq_rows) {
   constexpr int VEC = BF16 ? 8 : 4;
   constexpr int CH = 8;  // splits whose loads are in flight together
   const uint32_t tpr = D / VEC;  // threads per row
@@ -1271,18 +1369,27 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const void* __restrict_
   const uint32_t row = gid / tpr;
   const uint32_t d = (gid - row * tpr) * VEC;
   if (row >= rows) return;
+  uint32_t s_lo = 0, s_n = S;
+  size_t stride = rows, pbase = row;
+  if (tab) {
+    const uint32_t b = row / seq_rows;
+    s_lo = (uint32_t)tab[2 * b];
+    s_n = (uint32_t)tab[2 * b + 1];
+    stride = seq_rows;
+    pbase = row - b * seq_rows;
+  }
   // running merge (reference emax, weight sum, weighted sum), CH splits at a time
   float emax = kNegInf, wsum = 0.f;
   float acc[VEC];
 #pragma unroll
   for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
-  for (uint32_t s0 = 0; s0 < S; s0 += CH) {
+  for (uint32_t s0 = 0; s0 < s_n; s0 += CH) {
     float e[CH];
     float x[CH][VEC];
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      const bool in = s0 + j < S;
-      const size_t prow = (size_t)(in ? s0 + j : s0) * rows + row;
+      const bool in = s0 + j < s_n;
+      const size_t prow = (size_t)(s_lo + (in ? s0 + j : s0)) * stride + pbase;
       e[j] = in ? part_lse[prow] : kNegInf;
       if (BF16) {
         const uint4 raw = *reinterpret_cast<const uint4*>(reinterpret_cast<const u16*>(part_o) + prow * D + d);
@@ -1311,10 +1418,13 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const void* __restrict_
     emax = cmax;
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      const float wgt = __builtin_amdgcn_exp2f(e[j] - cmax);  // 0 for an empty or absent split
+      // an empty or absent split weighs exactly zero, whatever its partial
+      // slot holds (a split past its sequence's length does not write one)
+      const bool live = e[j] != kNegInf;
+      const float wgt = __builtin_amdgcn_exp2f(e[j] - cmax);
       wsum += wgt;
 #pragma unroll
-      for (int i = 0; i < VEC; ++i) acc[i] = fmaf(x[j][i], wgt, acc[i]);
+      for (int i = 0; i < VEC; ++i) acc[i] = fmaf(live ? x[j][i] : 0.f, wgt, acc[i]);
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
@@ -1340,12 +1450,14 @@ hipError_t launch_merge(const AttnParams& p, bool bf16, hipStream_t stream) {
   const size_t threads = rows * (p.D / (bf16 ? 8 : 4));
   if (threads > 0x7fffffff) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)((threads + 255) / 256);
+  const int32_t* tab = p.ragged ? p.split_tab : nullptr;
+  const uint32_t seq_rows = (uint32_t)((size_t)p.R * p.Hq);
   if (bf16)
     hipLaunchKernelGGL(attn_merge_kernel<true>, dim3(grid), dim3(256), 0, stream, p.part_o, p.part_lse, p.out, p.lse,
-                       (uint32_t)rows, (uint32_t)p.D, (uint32_t)p.S);
+                       (uint32_t)rows, (uint32_t)p.D, (uint32_t)p.S, tab, seq_rows);
   else
     hipLaunchKernelGGL(attn_merge_kernel<false>, dim3(grid), dim3(256), 0, stream, p.part_o, p.part_lse, p.out,
-                       p.lse, (uint32_t)rows, (uint32_t)p.D, (uint32_t)p.S);
+                       p.lse, (uint32_t)rows, (uint32_t)p.D, (uint32_t)p.S, tab, seq_rows);
   return hipGetLastError();
 }
 
@@ -1398,6 +1510,27 @@ AttnPlan plan_attn(int dtype, int B, int Hq, int Hkv, int D, int R, int max_len,
     base = (long)B * Hkv * M;
   }
   const int ntiles = (max_len + kBN - 1) / kBN;
+  // Batches of several sequences (bf16, no forced split count): the split
+  // slots are shared out on the device in proportion to each sequence's key
+  // tiles, so short sequences take few workgroups and long ones many, in one
+  // round of resident workgroups. TIDAR_ATTN_RAGGED=0 keeps one split count
+  // for every sequence instead.
+  const char* ragged_env = getenv("TIDAR_ATTN_RAGGED");
+  if (dtype == 1 && B > 1 && forced_splits == 0 && !(ragged_env && atoi(ragged_env) == 0)) {
+    const long slots = pl.waves == 8 ? 256 : 512;
+    long ns = slots / ((long)Hkv * pl.qtiles);
+    ns = std::min(ns, (long)B * (ntiles + local_tiles));
+    ns = std::min(ns, 0xffffL);
+    if (ns > B) {
+      pl.ragged = 1;
+      pl.S = (int)ns;
+      pl.chunk = 0;
+      pl.counter_bytes = ((size_t)B * 2 * sizeof(int32_t) + 255) / 256 * 256;
+      const size_t prow = (size_t)pl.S * R * Hq;
+      pl.ws_bytes = pl.counter_bytes + (prow * D * 2 + 255) / 256 * 256 + prow * sizeof(float);
+      return pl;
+    }
+  }
   int S;
   const char* target_env = getenv("TIDAR_ATTN_TARGET_WG");
   if (forced_splits > 0) {
@@ -1469,9 +1602,9 @@ hipError_t launch_attn_bf16(const AttnParams& p, hipStream_t stream) {
     if (e != hipSuccess || p.fused_merge) return e;
     return launch_merge(p, true, stream);
   }
-  const size_t grid = (size_t)p.B * p.Hkv * p.qtiles * p.S;
+  const size_t grid = (size_t)(p.ragged ? 1 : p.B) * p.Hkv * p.qtiles * p.S;
   if (grid > 0x7fffffff || p.qtiles > 0xffff || p.S > 0xffff || p.Hkv > 0xffff || p.g > 0xffff || p.k > 0xffff ||
-      p.block_len > 0xffff)
+      p.block_len > 0xffff || (p.ragged && (!p.split_tab || p.S <= p.B)))
     return hipErrorInvalidValue;
   const uint32_t qt_s = (uint32_t)p.qtiles | ((uint32_t)p.S << 16);
   const uint32_t hkv_g = (uint32_t)p.Hkv | ((uint32_t)p.g << 16);

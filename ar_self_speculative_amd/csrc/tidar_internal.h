@@ -19,8 +19,9 @@ struct AttnParams {
   float* lse;
   int32_t* dev_status;
   // split partials (S > 1 only): normalised output of each split over its
-  // keys, [S, B, R, Hq, D] in the input precision (bf16 or fp32), and its
-  // log-sum-exp in the log2 domain, [S, B, R, Hq] fp32 (-inf: no visible key)
+  // keys, [S, B, R, Hq, D] in the input precision (bf16 or fp32; ragged:
+  // [S, R, Hq, D]), and its log-sum-exp in the log2 domain, [S, B, R, Hq]
+  // fp32 (-inf: no visible key)
   void* part_o;
   float* part_lse;
   // decode path: arrival counters, one per (sequence, KV head), zero between
@@ -34,6 +35,14 @@ struct AttnParams {
   int waves;      // waves per workgroup (bf16 path)
   int decode;     // 1: the decode-regime kernel (few packed rows per KV head)
   int fused_merge;  // decode path: the last-arriving split merges (no merge kernel)
+  // ragged batches (B > 1, bf16 main kernel): S split slots per (KV head,
+  // query tile) are shared out among the sequences in proportion to their
+  // key tiles, on the device from the cache lengths; split s of sequence b
+  // then writes partial block start_b + s of [S, R, Hq] rows, and
+  // split_tab[b] = (start_b, S_b) tells the merge where they are
+  int ragged;
+  int local_tiles;    // step-key tiles of a sequence's last split (work weight)
+  int32_t* split_tab;  // [B, 2]
   float sm_scale;
   float scale_log2;  // sm_scale * log2(e)
 };
@@ -47,8 +56,9 @@ struct AttnPlan {
   int bm;          // packed query rows per workgroup
   int decode;      // decode-regime kernel: S prefix splits of `chunk` keys plus one split of step keys
   int fused_merge;
+  int ragged;      // split slots apportioned per sequence on the device (S = slots per KV head and query tile)
   size_t ws_bytes;
-  size_t counter_bytes;  // decode path: leading workspace bytes holding the arrival counters
+  size_t counter_bytes;  // leading workspace bytes: arrival counters (decode path) or the split table (ragged)
 };
 
 AttnPlan plan_attn(int dtype, int B, int Hq, int Hkv, int D, int R, int max_len, int forced_splits,

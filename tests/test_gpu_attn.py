@@ -190,6 +190,90 @@ def test_deterministic_and_split_independent():
     assert np.abs(one - a).max() <= 2 ** -7 and np.abs(many - a).max() <= 2 ** -7
 
 
+def test_empty_splits_of_short_sequences_leave_no_partial_to_read():
+    """Ragged batch with forced splits of 512 keys: the splits of the short
+    sequences that lie past their lengths exit early and write only an empty
+    log-sum-exp. The workspace is filled with NaN bytes first, so a merge that
+    read one of their (unwritten) partial slots would put NaN in the output."""
+    import ar_self_speculative_amd as tidar
+    from tests.gpu_util import attn_desc, dev_array, oracle_inputs
+    lens = [0, 5, 64, 700, 3000]
+    c = attn_case(dtype="bf16", layers=1, batch=len(lens), num_q_heads=8, num_kv_heads=2, head_dim=128, k=4,
+                  num_blocks=5, block_len=4, cache_len=lens, cache_capacity=max(lens) + 8, seed=21)
+    desc = attn_desc(c, num_splits=6)
+    args = [dev_array(c, n, 0) for n in ("q", "k_step", "v_step", "k_cache", "v_cache")]
+    ws = tidar.attn_workspace(desc)
+    ws.fill_(0xFF)
+    out = torch.empty_like(args[0])
+    lse = torch.empty(out.shape[:-1], dtype=torch.float32, device=out.device)
+    tidar.attn_step(desc, *args, torch.from_numpy(c.cache_len).cuda(), out, lse, None, ws)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    ref, rlse = oracle.attn_step(*oracle_inputs(c), c.cache_len, k=c.k, num_blocks=c.num_blocks,
+                                 block_len=c.block_len, sm_scale=c.sm_scale)
+    assert np.isfinite(got).all()
+    assert _report("ragged, empty splits, NaN workspace", got, ref, TOL["bf16"]) <= TOL["bf16"]
+    assert np.abs(lse.cpu().numpy() - rlse).max() <= LSE_TOL["bf16"]
+
+
+def _ragged_table(lens, slots, local_tiles, max_len):
+    """Host restatement of the device's split apportionment (start, count) per sequence."""
+    w = [(min(max(l, 0), max_len) + 63) // 64 + local_tiles for l in lens]
+    E = slots - len(lens)
+    c = -(-sum(w) // E)
+    tab, start = [], 0
+    for wi in w:
+        si = max(1, -(-wi // c))
+        tab.append((start, si))
+        start += si
+    assert start <= slots
+    return tab
+
+
+@pytest.mark.parametrize("lens", [[0, 5, 64, 700, 3000, 129, 1, 2048], [4096, 4096], [0, 0, 0]])
+def test_ragged_batch_split_apportionment(lens, monkeypatch):
+    """Batches of several sequences share the split slots out in proportion to
+    each sequence's key tiles. Checked: the split table the kernel leaves in the
+    workspace, every output row against the oracle (workspace filled with NaN
+    bytes first, so an unwritten partial that the merge read would show), and
+    agreement with one split count for all sequences (TIDAR_ATTN_RAGGED=0)."""
+    import ar_self_speculative_amd as tidar
+    from tests.gpu_util import attn_desc, dev_array
+    k, nb, bl = 4, 5, 4
+    c = attn_case(dtype="bf16", layers=1, batch=len(lens), num_q_heads=8, num_kv_heads=2, head_dim=128, k=k,
+                  num_blocks=nb, block_len=bl, cache_len=lens, cache_capacity=max(lens) + 8, seed=len(lens))
+    args = [dev_array(c, n, 0) for n in ("q", "k_step", "v_step", "k_cache", "v_cache")]
+    dlens = torch.from_numpy(c.cache_len).cuda()
+    outs = {}
+    for mode in ("ragged", "static"):
+        with monkeypatch.context() as mp:
+            mp.setenv("TIDAR_ATTN_RAGGED", "1" if mode == "ragged" else "0")
+            desc = attn_desc(c)
+            ws = tidar.attn_workspace(desc)  # None when one split needs no partials
+            if ws is not None:
+                ws.fill_(0xFF)
+            out = torch.empty_like(args[0])
+            lse = torch.empty(out.shape[:-1], dtype=torch.float32, device=out.device)
+            tidar.attn_step(desc, *args, dlens, out, lse, None, ws)
+            torch.cuda.synchronize()
+        if mode == "ragged":
+            # 512 slots over Hkv = 2 KV heads x 1 query tile, at most B x (tiles + local) of them
+            R = k + nb * bl
+            local = (k + 63) // 64 + (bl + 63) // 64
+            tiles = (max(lens) + 63) // 64
+            slots = min(512 // 2, len(lens) * (tiles + local))
+            tab = ws[: 8 * len(lens)].view(torch.int32).cpu().numpy().reshape(-1, 2)
+            assert [tuple(t) for t in tab.tolist()] == _ragged_table(lens, slots, local, max(lens))
+        outs[mode] = (out.float().cpu().numpy().astype(np.float64), lse.cpu().numpy())
+    ref, rlse = oracle.attn_step(*oracle_inputs(c), c.cache_len, k=c.k, num_blocks=c.num_blocks,
+                                 block_len=c.block_len, sm_scale=c.sm_scale)
+    for mode, (got, glse) in outs.items():
+        assert np.isfinite(got).all(), mode
+        assert _report(f"ragged {lens} {mode}", got, ref, TOL["bf16"]) <= TOL["bf16"]
+        assert np.abs(glse - rlse).max() <= LSE_TOL["bf16"]
+    assert np.abs(outs["ragged"][0] - outs["static"][0]).max() <= 2 ** -7
+
+
 def test_cache_len_beyond_bound_is_clamped_and_flagged():
     c = attn_case(dtype="bf16", layers=1, batch=1, num_q_heads=4, num_kv_heads=2, head_dim=128, k=4,
                   num_blocks=5, block_len=4, cache_len=100, cache_capacity=120, seed=5, poison=False)
