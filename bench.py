@@ -35,7 +35,18 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # on a device copy of known size. Valid only for the attention source it was
 # taken on (sha256 prefix of csrc/attn.hip); any other source reports null.
 ATTN_TRAFFIC = {
-    "8ca6ea5ef832f306": 57074936,
+    "4eb5f02a06b973bd": 57153946,
+}
+
+# MFMA utilisation of the main attention kernel at this workload, from a
+# rocprofv3 --pmc pass (SQ_VALU_MFMA_BUSY_CYCLES over 1024 * GRBM_GUI_ACTIVE / 8
+# XCDs), beside the same ratio for the MFMA-only ceiling kernel (a dependent
+# chain of v_mfma_f32_32x32x16_bf16, 96.9%). Keyed like ATTN_TRAFFIC; any other
+# attention source reports null.
+ATTN_COUNTERS = {
+    "4eb5f02a06b973bd": {"mfma_busy_frac": 0.2818, "ceiling_kernel_mfma_busy_frac": 0.9691,
+                         "mfma_busy_frac_of_ceiling": 0.2908, "valu_insts_per_mfma": 5.74,
+                         "mfma_coexec_frac": 0.4343, "wave_cycles_waiting_on_dependencies": 0.338},
 }
 
 SHAPE = dict(layers=36, batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128, P=4096, k=16,
@@ -220,6 +231,57 @@ def ceilings_bench(args) -> dict:
     return out
 
 
+def sampler_bench(args) -> None:
+    """The sampler alone (tidar_reject_sample) at one shape, B:k[:V] (V
+    defaults to the Qwen3 vocabulary 151936): 50 calls captured in a HIP
+    graph and replayed, HIP events on the launch stream. Inputs are the
+    sampler recipe drawn on the device (AR logits ~ N(0, 3), diffusion logits
+    = AR + N(0, 0.162), drafts by Gumbel-max from the diffusion logits).
+    Reports microseconds per call and the logit bytes the statistics pass
+    must read ((2k+1) V fp32 rows per sequence) per call time."""
+    import torch
+
+    import ar_self_speculative_amd as tidar
+    from tidar_synth import fill_verifier_device
+
+    parts = [int(x) for x in args.sampler.split(":")]
+    B, k = parts[0], parts[1]
+    V = parts[2] if len(parts) > 2 else 151936
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    ar = torch.empty(B, k + 1, V, dtype=torch.float32, device=dev)
+    diff = torch.empty(B, k, V, dtype=torch.float32, device=dev)
+    drafts = torch.empty(B, k, dtype=torch.int32, device=dev)
+    uni = torch.empty(B, k + 1, dtype=torch.float32, device=dev)
+    fill_verifier_device(ar, diff, drafts, uni, g, ar_sigma=3.0, diff_sigma=0.162)
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = torch.empty(tidar.reject_workspace_bytes(B, k, V), dtype=torch.uint8, device=dev)
+
+    def call():
+        tidar.reject_sample(ar_logits=ar, diff_logits=diff, drafts=drafts, uniforms=uni, accept_len=acc,
+                            next_token=nxt, dev_status=status, workspace=ws)
+
+    for _ in range(max(1, args.warmup)):
+        call()
+    calls = 50
+    graph = _capture(lambda: [call() for _ in range(calls)])
+    us = _time_graph(graph, max(1, args.steps // 5)) * 1e3 / calls
+    if int(status.item()):
+        print(f"device status flags set: {int(status.item())}", file=sys.stderr)
+        sys.exit(1)
+    logit_bytes = B * (2 * k + 1) * V * 4
+    print(json.dumps({
+        "metric": "sampler call time (tidar_reject_sample)", "value": round(us, 2), "unit": "us/call",
+        "higher_is_better": False, "n_gpus": 1, "data": "synthetic", "dtype": "f32",
+        "config": {"workload": f"rejection sampling, batch {B}, k={k}, vocab {V}", "batch": B, "k": k, "vocab": V},
+        "logit_bytes": logit_bytes, "logit_read_gbps": round(logit_bytes / (us * 1e-6) / 1e9, 1),
+        "mean_accept_len": round(float(acc.float().mean().item()), 3),
+    }), flush=True)
+
+
 def config5_bench(args) -> None:
     """Ragged batch at full depth: 8 sequences with prefixes from U{256..4096},
     k = 8 (80 query rows), 36 Qwen3-8B-shaped layers, 64 chained steps
@@ -240,7 +302,8 @@ def config5_bench(args) -> None:
     lens0 = config5_lengths(0)
     W = k * n_steps
     step = tidar.DecodeStep(layers=L, batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, k=k,
-                            cache_capacity=cap, max_cache_len=int(lens0.max()) + W, vocab=V)
+                            cache_capacity=cap, max_cache_len=int(lens0.max()) + W, vocab=V,
+                            num_splits=args.splits)
     R = step.R
     fill_device_step(step, seed=5, cache_len=lens0)
     dev = step.q.device
@@ -599,6 +662,8 @@ def main():
                     help="only time the ragged batch (8 sequences, k=8, 36 layers, 64 chained steps) and exit")
     ap.add_argument("--ceilings", action="store_true",
                     help="only measure the machine ceilings (HBM read, MFMA, exp/FMA rates, empty kernel) and exit")
+    ap.add_argument("--sampler", default="", metavar="B:k[:V]",
+                    help="only time the sampler (tidar_reject_sample) at batch B, draft length k, vocab V, and exit")
     ap.add_argument("--knee", action="store_true",
                     help="only run the append-prefill sweep, report its knee and the draft length it allows")
     args = ap.parse_args()
@@ -619,6 +684,9 @@ def main():
     if args.ceilings:
         print(json.dumps({"metric": "measured MI355X ceilings", "n_gpus": 1, "data": "synthetic",
                           **ceilings_bench(args)}), flush=True)
+        return
+    if args.sampler:
+        sampler_bench(args)
         return
     if args.knee:
         knee_bench(args)
@@ -713,6 +781,7 @@ def main():
                      "frac": round(achieved_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
                      "traffic": ATTN_TRAFFIC.get(attn_source_digest()),
                      "flops_per_launch": cnt["attn_flops_layer"]},
+        "mfma_util": ATTN_COUNTERS.get(attn_source_digest()),
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline()
