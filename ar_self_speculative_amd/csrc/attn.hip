@@ -121,6 +121,21 @@ __device__ __forceinline__ LocalRanges local_ranges(int r_lo, int r_hi, int k, i
   return lr;
 }
 
+__device__ __forceinline__ int wave_sum_int(int x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+// inclusive prefix sum over the wave's lanes
+__device__ __forceinline__ int wave_incl_scan_int(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
 __device__ __forceinline__ int remap_xcd(int i, int n) {
   // Workgroups are dealt to the 8 XCDs round-robin. Give each XCD a
   // contiguous range of work items so the query tiles that share a K/V chunk
@@ -548,7 +563,9 @@ __device__ __forceinline__ void tile_iter(Wave<D, NQT, LSE32>& st, lds_u8* __res
 // to a dword (each below 2^16, checked on the host): a_qt_s = qtiles | S << 16,
 // a_hkv_g = Hkv | g << 16, a_k_bl = k | block_len << 16; a_nwg is the grid size.
 
-template <int D, int NQT, int WAVES, bool LSE32>
+// RAG: ragged batch (split slots apportioned per sequence); a template
+// parameter so that single-length launches carry none of its code.
+template <int D, int NQT, int WAVES, bool LSE32, bool RAG>
 __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kernel(
     const int32_t* __restrict__ a_len, const void* __restrict__ a_q, const void* __restrict__ a_kc, uint32_t a_qt_s,
     uint32_t a_hkv_g, uint32_t a_k_bl, int a_R, int a_nwg, int a_cap, int a_chunk, int a_max_len, AttnParams p) {
@@ -580,12 +597,52 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
   w /= qtiles;
   int s, kvh, b, Sb, chunk, len = 0;
   size_t prow_off;  // partial rows of this split: [prow_off, prow_off + rows) of part_o / part_lse, in output rows
-  if (p.ragged) {
+  if (RAG && p.B <= 64) {
     // The sequence and split of slot `slot`: every workgroup shares the S
     // slots out the same way from the clamped lengths. Sequence i weighs
-    // w_i = its prefix tiles plus the step-key tiles of its last split; with
-    // c = ceil(sum w / (S - B)) it takes S_i = ceil(w_i / c) >= 1 slots
-    // (sum S_i <= S), and its splits cover ceil(tiles_i / S_i) tiles each.
+    // w_i = its prefix tiles plus the step-key tiles of its last split and
+    // takes S_i = max(1, ceil(w_i / c)) slots, c being the smallest tile
+    // count per split with sum S_i <= S (a binary search between
+    // ceil(sum w / S) and ceil(sum w / (S - B)), which always fits); its
+    // splits cover ceil(tiles_i / S_i) tiles each. Lane i holds sequence i.
+    const int slot = w % S;
+    kvh = w / S;
+    const int B = p.B, lt = p.local_tiles;
+    const int raw_l = lane < B ? a_len[lane] : 0;
+    const int li = min(max(raw_l, 0), a_max_len);
+    const int wl = lane < B ? (li + kBN - 1) / kBN + lt : 0;
+    const int wsum = __builtin_amdgcn_readfirstlane(wave_sum_int(wl));
+    int lo = max(1, (wsum + S - 1) / S), hi = (wsum + (S - B) - 1) / (S - B);
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      const int n = __builtin_amdgcn_readfirstlane(wave_sum_int(lane < B ? max(1, (wl + mid - 1) / mid) : 0));
+      if (n <= S)
+        hi = mid;
+      else
+        lo = mid + 1;
+    }
+    const int sl = lane < B ? max(1, (wl + lo - 1) / lo) : 0;
+    const int incl = wave_incl_scan_int(sl, lane);
+    if (qt == 0 && kvh == 0 && slot == 0 && wave == 0 && lane < B) {
+      p.split_tab[2 * lane] = incl - sl;
+      p.split_tab[2 * lane + 1] = sl;
+    }
+    const unsigned long long over = __ballot(lane < B && incl > slot);
+    if (over == 0) return;  // a slot no sequence needed
+    b = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(over));
+    Sb = __builtin_amdgcn_readlane(sl, b);
+    const int bstart = __builtin_amdgcn_readlane(incl, b) - Sb;
+    s = __builtin_amdgcn_readfirstlane(slot - bstart);
+    const int raw = __builtin_amdgcn_readlane(raw_l, b);
+    if (raw < 0 || raw > a_max_len) {
+      if (tid == 0 && p.dev_status) atomicOr(p.dev_status, 1);
+    }
+    len = __builtin_amdgcn_readlane(li, b);
+    chunk = __builtin_amdgcn_readfirstlane(((len + kBN - 1) / kBN + Sb - 1) / Sb * kBN);
+    prow_off = (size_t)(bstart + s - b) * a_R * Hkv * g;
+  } else if (RAG) {
+    // More than 64 sequences: the same sharing with c = ceil(sum w / (S - B))
+    // (sum S_i <= S), from a scalar pass over the lengths.
     const int slot = w % S;
     kvh = w / S;
     const int B = p.B, lt = p.local_tiles;
@@ -643,9 +700,9 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
   // there. (Ragged batches already know the length: no early copy.)
   const bool last = (s == Sb - 1);
   const int kbeg = s * chunk;
-  const int nk_hint = p.ragged ? 0
-                               : __builtin_amdgcn_readfirstlane(
-                                     max(0, (last ? a_max_len : min(kbeg + chunk, a_max_len)) - kbeg));
+  const int nk_hint = RAG ? 0
+                          : __builtin_amdgcn_readfirstlane(
+                                max(0, (last ? a_max_len : min(kbeg + chunk, a_max_len)) - kbeg));
   const size_t head_off = (size_t)(b * Hkv + kvh) * a_cap * D + (size_t)kbeg * D;
   const uint32_t pvo = copy_voff(lane, D * 2);
   if (nk_hint > 0)
@@ -679,7 +736,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
     st.l[nt] = 0.f;
   }
 
-  if (!p.ragged) {
+  if (!RAG) {
     len = __builtin_amdgcn_readfirstlane(a_len[b]);  // uniform: keeps the tile loop scalar
     if (len < 0 || len > a_max_len) {
       if (tid == 0 && p.dev_status) atomicOr(p.dev_status, 1);
@@ -689,12 +746,13 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
   const int kend = last ? len : min(kbeg + chunk, len);
   const int nk = max(0, kend - kbeg);
 
-  // A split that lies wholly past its sequence's length (ragged batches)
-  // has no keys: it records an empty partial (log-sum-exp -inf, which the
-  // merge weighs by exactly zero without reading the partial) and leaves,
-  // skipping the prologue's waits and the epilogue's 32 KB partial store.
-  // Its early K copy may still be in flight, so it waits for that first.
-  if (!last && nk == 0) {
+  // In a ragged batch a split can hold no prefix keys (a sequence shorter
+  // than its share of slots): it records an empty partial (log-sum-exp -inf,
+  // which the merge weighs by exactly zero without reading the partial) and
+  // leaves, skipping the prologue's waits and the epilogue's 32 KB partial
+  // store. (With one split count for every sequence such splits run through
+  // and store an all-zero partial, as every other split does.)
+  if (RAG && !last && nk == 0) {
     wait_copies();
     if (half == 0) {
       const __amdgpu_buffer_rsrc_t lrsrc = make_rsrc(p.part_lse + prow_off, 0xFFFFFFFFu);
@@ -1350,12 +1408,12 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p) {
 // O = sum_s w_s o_s / sum_s w_s and LSE = max e + log2(sum_s w_s).
 // One thread per 8 (bf16) or 4 (fp32) output elements of a row.
 // ---------------------------------------------------------------------------
-template <bool BF16>
 // Arguments are plain scalars so that they are preloaded into scalar registers
 // at dispatch and the partial loads need not wait for the argument block.
-// Split partials of an output row: with tab (ragged batches), sequence b's
+// Split partials of an output row: with RAG (ragged batches), sequence b's
 // splits sit in partial blocks tab[2b] .. tab[2b] + tab[2b+1] - 1 of
 // seq_rows rows each; without, split s of every row is block s of `rows`.
+template <bool BF16, bool RAG>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const void* __restrict__ part_o,
                                                         const float* __restrict__ part_lse, void* __restrict__ out,
                                                         float* __restrict__ lse, uint32_t rows, uint32_t D,
@@ -1371,7 +1429,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const void* __restrict_
   if (row >= rows) return;
   uint32_t s_lo = 0, s_n = S;
   size_t stride = rows, pbase = row;
-  if (tab) {
+  if (RAG) {
     const uint32_t b = row / seq_rows;
     s_lo = (uint32_t)tab[2 * b];
     s_n = (uint32_t)tab[2 * b + 1];
@@ -1418,11 +1476,11 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const void* __restrict_
     emax = cmax;
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      // an empty or absent split weighs exactly zero, whatever its partial
-      // slot holds (a split past its sequence's length does not write one)
-      const bool live = e[j] != kNegInf;
-      const float wgt = __builtin_amdgcn_exp2f(e[j] - cmax);
+      const float wgt = __builtin_amdgcn_exp2f(e[j] - cmax);  // 0 for an empty or absent split
       wsum += wgt;
+      // in a ragged batch an empty split writes no partial: weigh it by
+      // exactly zero, whatever its partial slot holds
+      const bool live = !RAG || e[j] != kNegInf;
 #pragma unroll
       for (int i = 0; i < VEC; ++i) acc[i] = fmaf(live ? x[j][i] : 0.f, wgt, acc[i]);
     }
@@ -1452,12 +1510,15 @@ hipError_t launch_merge(const AttnParams& p, bool bf16, hipStream_t stream) {
   const unsigned grid = (unsigned)((threads + 255) / 256);
   const int32_t* tab = p.ragged ? p.split_tab : nullptr;
   const uint32_t seq_rows = (uint32_t)((size_t)p.R * p.Hq);
-  if (bf16)
-    hipLaunchKernelGGL(attn_merge_kernel<true>, dim3(grid), dim3(256), 0, stream, p.part_o, p.part_lse, p.out, p.lse,
-                       (uint32_t)rows, (uint32_t)p.D, (uint32_t)p.S, tab, seq_rows);
-  else
-    hipLaunchKernelGGL(attn_merge_kernel<false>, dim3(grid), dim3(256), 0, stream, p.part_o, p.part_lse, p.out,
+  if (bf16 && tab)
+    hipLaunchKernelGGL((attn_merge_kernel<true, true>), dim3(grid), dim3(256), 0, stream, p.part_o, p.part_lse, p.out,
                        p.lse, (uint32_t)rows, (uint32_t)p.D, (uint32_t)p.S, tab, seq_rows);
+  else if (bf16)
+    hipLaunchKernelGGL((attn_merge_kernel<true, false>), dim3(grid), dim3(256), 0, stream, p.part_o, p.part_lse, p.out,
+                       p.lse, (uint32_t)rows, (uint32_t)p.D, (uint32_t)p.S, tab, seq_rows);
+  else
+    hipLaunchKernelGGL((attn_merge_kernel<false, false>), dim3(grid), dim3(256), 0, stream, p.part_o, p.part_lse,
+                       p.out, p.lse, (uint32_t)rows, (uint32_t)p.D, (uint32_t)p.S, tab, seq_rows);
   return hipGetLastError();
 }
 
@@ -1614,8 +1675,15 @@ hipError_t launch_attn_bf16(const AttnParams& p, hipStream_t stream) {
   // 128 query rows per workgroup (four waves of 32 rows), or 256 (eight
   // waves, head_dim 128); the row sums in fp32 when the caller wants the LSE
   const bool l32 = p.lse != nullptr;
-#define TIDAR_LAUNCH(D_, W_, L_) \
-  hipLaunchKernelGGL((attn_bf16_kernel<D_, 1, W_, L_>), dim3((unsigned)grid), dim3(64 * W_), 0, stream, TIDAR_ATTN_ARGS)
+#define TIDAR_LAUNCH1(D_, W_, L_, R_) \
+  hipLaunchKernelGGL((attn_bf16_kernel<D_, 1, W_, L_, R_>), dim3((unsigned)grid), dim3(64 * W_), 0, stream, TIDAR_ATTN_ARGS)
+#define TIDAR_LAUNCH(D_, W_, L_)        \
+  do {                                  \
+    if (p.ragged)                       \
+      TIDAR_LAUNCH1(D_, W_, L_, true);  \
+    else                                \
+      TIDAR_LAUNCH1(D_, W_, L_, false); \
+  } while (0)
   if (p.D == 128 && p.waves == 8) {
     if (l32) TIDAR_LAUNCH(128, 8, true); else TIDAR_LAUNCH(128, 8, false);
   } else if (p.D == 128 && p.waves == 4) {
@@ -1626,6 +1694,7 @@ hipError_t launch_attn_bf16(const AttnParams& p, hipStream_t stream) {
     return hipErrorInvalidValue;
   }
 #undef TIDAR_LAUNCH
+#undef TIDAR_LAUNCH1
 #undef TIDAR_ATTN_ARGS
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.S == 1) return e;

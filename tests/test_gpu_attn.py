@@ -190,11 +190,12 @@ def test_deterministic_and_split_independent():
     assert np.abs(one - a).max() <= 2 ** -7 and np.abs(many - a).max() <= 2 ** -7
 
 
-def test_empty_splits_of_short_sequences_leave_no_partial_to_read():
-    """Ragged batch with forced splits of 512 keys: the splits of the short
-    sequences that lie past their lengths exit early and write only an empty
-    log-sum-exp. The workspace is filled with NaN bytes first, so a merge that
-    read one of their (unwritten) partial slots would put NaN in the output."""
+def test_forced_splits_past_short_sequences_on_a_nan_workspace():
+    """Ragged batch with forced splits of 512 keys (one split count for every
+    sequence): the splits of the short sequences that lie past their lengths
+    hold no keys. The workspace is filled with NaN bytes first, so an empty
+    split that left its partial slot unwritten, or a merge that mixed one in,
+    would put NaN in the output."""
     import ar_self_speculative_amd as tidar
     from tests.gpu_util import attn_desc, dev_array, oracle_inputs
     lens = [0, 5, 64, 700, 3000]
@@ -217,10 +218,11 @@ def test_empty_splits_of_short_sequences_leave_no_partial_to_read():
 
 
 def _ragged_table(lens, slots, local_tiles, max_len):
-    """Host restatement of the device's split apportionment (start, count) per sequence."""
+    """Host restatement of the device's split apportionment (start, count) per
+    sequence: the smallest tiles-per-split c whose counts fit the slots."""
     w = [(min(max(l, 0), max_len) + 63) // 64 + local_tiles for l in lens]
-    E = slots - len(lens)
-    c = -(-sum(w) // E)
+    count = lambda c: sum(max(1, -(-wi // c)) for wi in w)
+    c = next(c for c in range(1, sum(w) + 1) if count(c) <= slots)
     tab, start = [], 0
     for wi in w:
         si = max(1, -(-wi // c))
