@@ -525,6 +525,20 @@ __device__ __forceinline__ void main_iter(Wave<D, NQT, LSE32>& st, lds_u8* __res
   wait_copies();
 }
 
+// The copies of main-loop iteration t alone, for a wave with no rows to
+// compute: the same instructions as main_iter issues, so every tile still
+// arrives whole.
+template <int D, int WAVES>
+__device__ __forceinline__ void main_iter_copies(lds_u8* __restrict__ kb_dst, lds_u8* __restrict__ vb_dst,
+                                                 const TileSeq& seq, int t, int wave) {
+  if (t + 2 < seq.count()) {
+    const TileSrc a = seq.at(t + 2);
+    copy_tile<D, WAVES>(make_rsrc(a.k, a.bytes), a.vo, a.row0, a.row_bytes, kb_dst, wave);
+  }
+  copy_tile<D, WAVES>(make_rsrc(seq.pv, seq.pbytes), seq.pvo, (t + 1) * kBN, seq.prb, vb_dst, wave);
+  wait_copies();
+}
+
 // One iteration t of the tile loop: copies of K[t+2] (into kb_dst) and
 // V[t+1] (into vb_dst) are issued, then the tile step runs on K[t+1]
 // (kb_next) and V[t] (vb_cur). The four buffers are distinct; passing them as
@@ -537,7 +551,8 @@ __device__ __forceinline__ void tile_iter(Wave<D, NQT, LSE32>& st, lds_u8* __res
                                           const lds_u8* __restrict__ kb_next, const lds_u8* __restrict__ vb_cur,
                                           lds_u8* __restrict__ vb_dst, const TileSeq& seq, int t, int wave, int lane,
                                           const RowRule (&rules)[NQT], float sl2,
-                                          typename Wave<D, NQT, LSE32>::S& sA, typename Wave<D, NQT, LSE32>::S& sB) {
+                                          typename Wave<D, NQT, LSE32>::S& sA, typename Wave<D, NQT, LSE32>::S& sB,
+                                          bool live) {
   // t + 1 < count(): the next tile exists (the caller peels the last tile)
   if (t + 2 < seq.count()) {
     const TileSrc a = seq.at(t + 2);
@@ -545,7 +560,8 @@ __device__ __forceinline__ void tile_iter(Wave<D, NQT, LSE32>& st, lds_u8* __res
   }
   const TileSrc n = seq.at(t + 1);
   copy_tile<D, WAVES>(make_rsrc(n.v, n.bytes), n.vo, n.row0, n.row_bytes, vb_dst, wave);
-  st.template step<true, true, true>(kb_next, vb_cur, sA, sB, sl2, n.local, n.nvalid, n.c_base, lane, &rules);
+  if (live)
+    st.template step<true, true, true>(kb_next, vb_cur, sA, sB, sl2, n.local, n.nvalid, n.c_base, lane, &rules);
 #pragma unroll
   for (int nt = 0; nt < NQT; ++nt) {
     sA[nt][0] = sB[nt][0];
@@ -563,9 +579,10 @@ __device__ __forceinline__ void tile_iter(Wave<D, NQT, LSE32>& st, lds_u8* __res
 // to a dword (each below 2^16, checked on the host): a_qt_s = qtiles | S << 16,
 // a_hkv_g = Hkv | g << 16, a_k_bl = k | block_len << 16; a_nwg is the grid size.
 
-// RAG: ragged batch (split slots apportioned per sequence); a template
-// parameter so that single-length launches carry none of its code.
-template <int D, int NQT, int WAVES, bool LSE32, bool RAG>
+// RAG: ragged batch (split slots apportioned per sequence); PAD: the last
+// query tile is only partly filled. Template parameters, so that launches
+// without them carry none of their code.
+template <int D, int NQT, int WAVES, bool LSE32, bool RAG, bool PAD>
 __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kernel(
     const int32_t* __restrict__ a_len, const void* __restrict__ a_q, const void* __restrict__ a_kc, uint32_t a_qt_s,
     uint32_t a_hkv_g, uint32_t a_k_bl, int a_R, int a_nwg, int a_cap, int a_chunk, int a_max_len, AttnParams p) {
@@ -714,6 +731,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
   // bounds) and are zeroed, which keeps the eight loads free of branches.
   const int M = a_R * g;
   const int Hq = Hkv * g;
+  // A wave whose rows all lie past M (the padded part of the last query
+  // tile) skips the matrix and softmax work; it still issues its share of the
+  // tile copies and takes part in every barrier.
+  const bool live = !PAD || qt * BM + wave * WROWS < M;
   W st;
   st.init_addr(lane);
   RowRule rules[NQT];
@@ -834,12 +855,14 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
       const TileSrc t1 = seq.at(1);
       copy_tile<D, WAVES>(make_rsrc(t1.k, t1.bytes), t1.vo, t1.row0, t1.row_bytes, KB[1], wave);
     }
-    st.qk(KB[0], sA);
-    if (t0.local)
-      W::template mask<true>(sA, lane, t0.nvalid, t0.c_base, rules);
-    else if (t0.nvalid < kBN)
-      W::template mask<false>(sA, lane, t0.nvalid, 0, rules);
-    st.tile_max(sA, sl2);
+    if (live) {
+      st.qk(KB[0], sA);
+      if (t0.local)
+        W::template mask<true>(sA, lane, t0.nvalid, t0.c_base, rules);
+      else if (t0.nvalid < kBN)
+        W::template mask<false>(sA, lane, t0.nvalid, 0, rules);
+      st.tile_max(sA, sl2);
+    }
     wait_copies();
   }
   if (ntot == 0) wait_copies();  // the early copy lands before KB[0] is reused for staging
@@ -850,31 +873,40 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
   // barrier: all reads of K[t] (QK^T of tile t) and V[t-1] (PV of tile t-1)
   // are done before this iteration's copies overwrite their buffers.
   int t = 0;
-  for (; t + 1 < tmain; t += 2) {
-    __syncthreads();
-    main_iter<D, NQT, WAVES, LSE32>(st, KB[0], KB[1], VB[0], VB[1], seq, t, wave, sl2, sA, sB);
-    __syncthreads();
-    main_iter<D, NQT, WAVES, LSE32>(st, KB[1], KB[0], VB[1], VB[0], seq, t + 1, wave, sl2, sB, sA);
-  }
-  if (t < tmain) {  // an odd count: one more (t even), then the scores move back to sA
-    __syncthreads();
-    main_iter<D, NQT, WAVES, LSE32>(st, KB[0], KB[1], VB[0], VB[1], seq, t, wave, sl2, sA, sB);
-#pragma unroll
-    for (int nt = 0; nt < NQT; ++nt) {
-      sA[nt][0] = sB[nt][0];
-      sA[nt][1] = sB[nt][1];
+  if (live) {
+    for (; t + 1 < tmain; t += 2) {
+      __syncthreads();
+      main_iter<D, NQT, WAVES, LSE32>(st, KB[0], KB[1], VB[0], VB[1], seq, t, wave, sl2, sA, sB);
+      __syncthreads();
+      main_iter<D, NQT, WAVES, LSE32>(st, KB[1], KB[0], VB[1], VB[0], seq, t + 1, wave, sl2, sB, sA);
     }
-    ++t;
+    if (t < tmain) {  // an odd count: one more (t even), then the scores move back to sA
+      __syncthreads();
+      main_iter<D, NQT, WAVES, LSE32>(st, KB[0], KB[1], VB[0], VB[1], seq, t, wave, sl2, sA, sB);
+#pragma unroll
+      for (int nt = 0; nt < NQT; ++nt) {
+        sA[nt][0] = sB[nt][0];
+        sA[nt][1] = sB[nt][1];
+      }
+      ++t;
+    }
+  } else {
+    // the same barriers and copies, no compute (a loop of its own, so the
+    // computing waves' loop carries no branch)
+    for (; t < tmain; ++t) {
+      __syncthreads();
+      main_iter_copies<D, WAVES>((t & 1) ? KB[1] : KB[0], (t & 1) ? VB[0] : VB[1], seq, t, wave);
+    }
   }
   for (; t + 1 < ntot; ++t) {
     const int par = t & 1;
     __syncthreads();
     tile_iter<D, NQT, WAVES, LSE32>(st, par ? KB[1] : KB[0], par ? KB[0] : KB[1], par ? VB[1] : VB[0],
-                             par ? VB[0] : VB[1], seq, t, wave, lane, rules, sl2, sA, sB);
+                             par ? VB[0] : VB[1], seq, t, wave, lane, rules, sl2, sA, sB, live);
   }
   if (t < ntot) {  // the last tile: P V only (its V is in VB[t & 1])
     __syncthreads();
-    st.template step<false, false>(nullptr, (t & 1) ? VB[1] : VB[0], sA, sB, sl2);
+    if (live) st.template step<false, false>(nullptr, (t & 1) ? VB[1] : VB[0], sA, sB, sl2);
   }
 
   // o[nt][dt][v] holds O^T[d = 32*dt + 8*(v/4) + 4*half + v%4][this lane's row].
@@ -1675,8 +1707,16 @@ hipError_t launch_attn_bf16(const AttnParams& p, hipStream_t stream) {
   // 128 query rows per workgroup (four waves of 32 rows), or 256 (eight
   // waves, head_dim 128); the row sums in fp32 when the caller wants the LSE
   const bool l32 = p.lse != nullptr;
-#define TIDAR_LAUNCH1(D_, W_, L_, R_) \
-  hipLaunchKernelGGL((attn_bf16_kernel<D_, 1, W_, L_, R_>), dim3((unsigned)grid), dim3(64 * W_), 0, stream, TIDAR_ATTN_ARGS)
+#define TIDAR_LAUNCH2(D_, W_, L_, R_, P_)                                                                        \
+  hipLaunchKernelGGL((attn_bf16_kernel<D_, 1, W_, L_, R_, P_>), dim3((unsigned)grid), dim3(64 * W_), 0, stream, \
+                     TIDAR_ATTN_ARGS)
+#define TIDAR_LAUNCH1(D_, W_, L_, R_)          \
+  do {                                         \
+    if (pad)                                   \
+      TIDAR_LAUNCH2(D_, W_, L_, R_, true);     \
+    else                                       \
+      TIDAR_LAUNCH2(D_, W_, L_, R_, false);    \
+  } while (0)
 #define TIDAR_LAUNCH(D_, W_, L_)        \
   do {                                  \
     if (p.ragged)                       \
@@ -1684,6 +1724,8 @@ hipError_t launch_attn_bf16(const AttnParams& p, hipStream_t stream) {
     else                                \
       TIDAR_LAUNCH1(D_, W_, L_, false); \
   } while (0)
+  // packed query rows that leave the last tile (32 rows per wave) partly empty
+  const bool pad = ((size_t)p.R * p.g) % (size_t)(32 * p.waves * p.nqt) != 0;
   if (p.D == 128 && p.waves == 8) {
     if (l32) TIDAR_LAUNCH(128, 8, true); else TIDAR_LAUNCH(128, 8, false);
   } else if (p.D == 128 && p.waves == 4) {
@@ -1695,6 +1737,7 @@ hipError_t launch_attn_bf16(const AttnParams& p, hipStream_t stream) {
   }
 #undef TIDAR_LAUNCH
 #undef TIDAR_LAUNCH1
+#undef TIDAR_LAUNCH2
 #undef TIDAR_ATTN_ARGS
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.S == 1) return e;
