@@ -40,7 +40,7 @@ EXPORTS = (
     "tidar_logprob_workspace_bytes", "tidar_token_logprobs",
     # measurement kernels (include/tidar_ceilings.h)
     "tidar_ceiling_hbm_read", "tidar_ceiling_mfma_bf16", "tidar_ceiling_exp_f32", "tidar_ceiling_fma_f32",
-    "tidar_ceiling_empty",
+    "tidar_ceiling_lds_read_b128", "tidar_ceiling_lds_read_tr16", "tidar_ceiling_empty",
 )
 
 
@@ -94,7 +94,8 @@ def load() -> ctypes.CDLL:
     lib.tidar_reject_noalloc_max_bytes.argtypes = []
     lib.tidar_ceiling_hbm_read.restype = ctypes.c_int
     lib.tidar_ceiling_hbm_read.argtypes = [vp, sz, ctypes.c_int, vp, vp]
-    for name in ("tidar_ceiling_mfma_bf16", "tidar_ceiling_exp_f32", "tidar_ceiling_fma_f32"):
+    for name in ("tidar_ceiling_mfma_bf16", "tidar_ceiling_exp_f32", "tidar_ceiling_fma_f32",
+                 "tidar_ceiling_lds_read_b128", "tidar_ceiling_lds_read_tr16"):
         getattr(lib, name).restype = ctypes.c_int
         getattr(lib, name).argtypes = [ctypes.c_int, ctypes.c_int, vp, vp]
     lib.tidar_ceiling_empty.restype = ctypes.c_int
@@ -269,7 +270,8 @@ def token_logprobs(*, logits, targets, logprobs, workspace, dev_status=None, str
 def ceiling(name: str, *args, stream=None):
     """Enqueue one measurement kernel of include/tidar_ceilings.h:
     ceiling("hbm_read", src_tensor, grid, sink), ceiling("mfma_bf16", grid, iters, sink),
-    ceiling("exp_f32" | "fma_f32", grid, iters, sink), ceiling("empty", grid)."""
+    ceiling("exp_f32" | "fma_f32" | "lds_read_b128" | "lds_read_tr16", grid, iters, sink),
+    ceiling("empty", grid)."""
     st = _stream(stream)
     if name == "hbm_read":
         src, grid, sink = args

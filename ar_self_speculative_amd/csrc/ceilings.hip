@@ -1,7 +1,7 @@
 // Measured ceilings of the MI355X (gfx950) for the roofline of the decode
-// step: HBM streaming-read bandwidth, the bf16 MFMA rate, the fp32
-// exponential and FMA issue rates, and the cost of one empty kernel in a
-// stream or graph. These are measurement kernels, not part of the decode
+// step: HBM streaming-read bandwidth, the bf16 MFMA rate, the LDS read rate
+// (plain and transposing reads), the fp32 exponential and FMA issue rates,
+// and the cost of one empty kernel in a stream or graph. These are measurement kernels, not part of the decode
 // step; bench.py times them with events on the stream they are launched on.
 #include "tidar_ceilings.h"
 
@@ -90,6 +90,49 @@ __global__ __launch_bounds__(256) void fma_kernel(int iters, float a, float b, f
   if (s == -1.2345f) sink[0] = s;
 }
 
+// LDS read rate: each wave streams reads from a 64 KB LDS buffer (filled
+// once), eight independent reads per iteration folded into xors, so the loads
+// stay live. TR = false: ds_read_b128 (16 bytes per lane, consecutive lanes
+// consecutive); TR = true: the transposing ds_read_b64_tr_b16 (8 bytes per
+// lane) that the attention kernel's V fragments use. Offsets stay inside the
+// buffer (masked to 64 KB, multiples of the access size).
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+constexpr uint32_t kLdsBytes = 65536;
+template <bool TR>
+__global__ __launch_bounds__(256) void lds_read_kernel(int iters, uint32_t* __restrict__ sink) {
+  __shared__ __attribute__((aligned(16))) uint8_t buf[kLdsBytes];
+  typedef __attribute__((address_space(3))) uint8_t lds8;
+  lds8* const base = (lds8*)buf;
+  for (uint32_t i = threadIdx.x; i < kLdsBytes / 4; i += 256)
+    *reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(base + 4 * i) = i * 2654435761u;
+  __syncthreads();
+  const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr uint32_t kStep = TR ? 512u : 1024u;  // bytes one wave reads per instruction
+  constexpr uint32_t kLane = TR ? 8u : 16u;
+  uint32_t acc = 0;
+  u32x4 a4[8] = {};
+  s16x4 a2[8] = {};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t off = (((uint32_t)it * 8u + (uint32_t)j) * kStep + wave * 4096u + lane * kLane) & (kLdsBytes - 1);
+      if (TR)
+        a2[j] ^= __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(base + off));
+      else
+        a4[j] ^= *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(base + off);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    // 16-bit halves packed into full 32-bit words, so the folded value can
+    // take any 32-bit pattern and the reads stay live
+    const uint32_t lo = (uint32_t)(uint16_t)a2[j][0] | ((uint32_t)(uint16_t)a2[j][1] << 16);
+    const uint32_t hi = (uint32_t)(uint16_t)a2[j][2] | ((uint32_t)(uint16_t)a2[j][3] << 16);
+    acc ^= TR ? (lo ^ hi) : (a4[j][0] ^ a4[j][1] ^ a4[j][2] ^ a4[j][3]);
+  }
+  if (acc == 0x9e3779b9u) sink[0] = acc;
+}
+
 __global__ void empty_kernel() {}
 
 }  // namespace
@@ -107,6 +150,20 @@ int tidar_ceiling_hbm_read(const void* src, size_t bytes, int grid, uint32_t* si
 int tidar_ceiling_mfma_bf16(int grid, int iters, float* sink, void* stream) {
   if (!sink || grid < 1 || iters < 1) return -1;
   hipLaunchKernelGGL(mfma_kernel, dim3((unsigned)grid), dim3(256), 0, static_cast<hipStream_t>(stream), iters, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+int tidar_ceiling_lds_read_b128(int grid, int iters, uint32_t* sink, void* stream) {
+  if (!sink || grid < 1 || iters < 1) return -1;
+  hipLaunchKernelGGL(lds_read_kernel<false>, dim3((unsigned)grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     iters, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+int tidar_ceiling_lds_read_tr16(int grid, int iters, uint32_t* sink, void* stream) {
+  if (!sink || grid < 1 || iters < 1) return -1;
+  hipLaunchKernelGGL(lds_read_kernel<true>, dim3((unsigned)grid), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     iters, sink);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

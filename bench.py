@@ -172,7 +172,8 @@ def _capture(fn):
 
 def ceilings_bench(args) -> dict:
     """Measured machine ceilings: HBM streaming read, bf16 MFMA rate, fp32
-    exponential and FMA issue rates, and the cost of an empty kernel launched
+    exponential and FMA issue rates, LDS read rates (ds_read_b128 and the
+    transposing ds_read_b64_tr_b16), and the cost of an empty kernel launched
     back to back (from a graph and from the stream). Each kernel is timed with
     HIP events on the stream it is launched on."""
     import torch
@@ -221,6 +222,14 @@ def ceilings_bench(args) -> dict:
     clk = out["mfma_implied_clock_ghz"] * 1e9
     out["exp_f32_cycles_per_wave_instr"] = round(1024 * clk * 64 / (n / t_exp), 2)
     out["fma_f32_cycles_per_wave_instr"] = round(1024 * clk * 64 / (n / t_fma), 2)
+    # LDS reads: two 256-thread workgroups per CU (8 waves), bytes per clock
+    # per CU at the clock implied by the MFMA run
+    grid, iters = 512, 4096
+    for kind, lane_bytes in (("lds_read_b128", 16), ("lds_read_tr16", 8)):
+        t = timed(lambda: tidar.ceiling(kind, grid, iters, sink), 3)
+        nb = grid * 256 * 8 * iters * lane_bytes
+        out[f"{kind}_tbps"] = round(nb / t / 1e12, 1)
+        out[f"{kind}_bytes_per_clk_per_cu"] = round(nb / t / (256 * clk), 1)
     for grid in (1, 512):
         def many():
             for _ in range(100):

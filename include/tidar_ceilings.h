@@ -1,7 +1,8 @@
 /*
  * tidar_ceilings.h - measurement kernels of libtidar: the machine ceilings
  * that the decode step's rooflines are stated against (HBM streaming read,
- * bf16 MFMA rate, fp32 exponential and FMA issue rates, one empty kernel).
+ * bf16 MFMA rate, LDS read rate, fp32 exponential and FMA issue rates, one
+ * empty kernel).
  * They compute nothing of the method; bench.py times them with HIP events on
  * the stream they are enqueued on.
  *
@@ -28,6 +29,13 @@ int tidar_ceiling_hbm_read(const void* src, size_t bytes, int grid, uint32_t* si
  * v_mfma_f32_32x32x16_bf16 (32768 flops each) on four independent chains:
  * grid * 4 * 4 * iters * 32768 flops in all. `sink`: one device float. */
 int tidar_ceiling_mfma_bf16(int grid, int iters, float* sink, void* stream);
+
+/* `grid` workgroups of 256 threads, each with a 64 KB LDS buffer (two fit
+ * on a CU): every wave issues 8 * iters LDS reads, ds_read_b128 (16 bytes per
+ * lane: grid * 256 * 8 * iters * 16 bytes in all) or the transposing
+ * ds_read_b64_tr_b16 (8 bytes per lane). `sink`: one device uint32. */
+int tidar_ceiling_lds_read_b128(int grid, int iters, uint32_t* sink, void* stream);
+int tidar_ceiling_lds_read_tr16(int grid, int iters, uint32_t* sink, void* stream);
 
 /* `grid` workgroups of 256 threads; each thread evaluates 8 * iters fp32
  * base-2 exponentials (v_exp_f32) on eight independent chains. */
