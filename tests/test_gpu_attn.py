@@ -222,7 +222,10 @@ def _ragged_table(lens, slots, local_tiles, max_len):
     sequence: the smallest tiles-per-split c whose counts fit the slots."""
     w = [(min(max(l, 0), max_len) + 63) // 64 + local_tiles for l in lens]
     count = lambda c: sum(max(1, -(-wi // c)) for wi in w)
-    c = next(c for c in range(1, sum(w) + 1) if count(c) <= slots)
+    if len(lens) <= 64:
+        c = next(c for c in range(1, sum(w) + 1) if count(c) <= slots)
+    else:  # more sequences than a wave's lanes: c = ceil(sum w / (slots - B))
+        c = -(-sum(w) // (slots - len(lens)))
     tab, start = [], 0
     for wi in w:
         si = max(1, -(-wi // c))
@@ -232,7 +235,11 @@ def _ragged_table(lens, slots, local_tiles, max_len):
     return tab
 
 
-@pytest.mark.parametrize("lens", [[0, 5, 64, 700, 3000, 129, 1, 2048], [4096, 4096], [0, 0, 0]])
+_MANY = [int(x) for x in np.random.default_rng(70).integers(0, 400, size=70)]
+
+
+@pytest.mark.parametrize("lens", [[0, 5, 64, 700, 3000, 129, 1, 2048], [4096, 4096], [0, 0, 0], _MANY],
+                         ids=["mixed", "equal", "empty", "70seq"])
 def test_ragged_batch_split_apportionment(lens, monkeypatch):
     """Batches of several sequences share the split slots out in proportion to
     each sequence's key tiles. Checked: the split table the kernel leaves in the
@@ -273,7 +280,10 @@ def test_ragged_batch_split_apportionment(lens, monkeypatch):
         assert np.isfinite(got).all(), mode
         assert _report(f"ragged {lens} {mode}", got, ref, TOL["bf16"]) <= TOL["bf16"]
         assert np.abs(glse - rlse).max() <= LSE_TOL["bf16"]
-    assert np.abs(outs["ragged"][0] - outs["static"][0]).max() <= 2 ** -7
+    # the two plans merge differently rounded bf16 partials: they agree to a
+    # bf16 ulp or two of each output (2^-7 relative per ulp)
+    diff = np.abs(outs["ragged"][0] - outs["static"][0])
+    assert (diff <= 2 ** -6 * np.maximum(1.0, np.abs(ref))).all(), float(diff.max())
 
 
 def test_cache_len_beyond_bound_is_clamped_and_flagged():
