@@ -96,7 +96,11 @@ int tidar_version(void);
  * separately and merged by log-sum-exp; the result does not depend on the
  * split count beyond floating-point rounding. Each split's normalised output
  * is held in the workspace in the input precision (bf16 or fp32), with its
- * log-sum-exp in fp32. An optional decode-regime kernel (few packed query
+ * log-sum-exp in fp32. With several sequences (batch > 1, bf16, num_splits =
+ * 0) the pieces are shared out per sequence on the device, in proportion to
+ * each sequence's cache_len, so a ragged batch runs in one round of
+ * workgroups; the per-sequence split table lives at the start of the
+ * workspace and is rewritten by every launch. An optional decode-regime kernel (few packed query
  * rows per KV head, see tidar_attn_workspace_bytes) streams 128-key splits
  * plus one split of the step's keys, and the split that finishes last merges
  * them when they are small enough.
@@ -113,7 +117,8 @@ typedef struct {
   int32_t max_cache_len;   /* host-known bound on cache_len[b], <= cap; used to plan splits */
   float sm_scale;          /* softmax scale, > 0 (typically 1/sqrt(D)) */
   int32_t dtype;           /* TIDAR_DTYPE_F32 or TIDAR_DTYPE_BF16 for q, k/v, out */
-  int32_t num_splits;      /* 0 = library chooses; otherwise the prefix split count */
+  int32_t num_splits;      /* 0 = library chooses; otherwise the prefix split count (the same
+                              for every sequence) */
 } tidar_attn_desc;
 
 /* Workspace bytes tidar_attn_step needs for this descriptor (0 if none).
