@@ -69,23 +69,7 @@ __device__ __forceinline__ int wave_max_i(int x) {
   return x;
 }
 
-// Block reductions with a fixed combination order (waves 0..3 in sequence).
-__device__ __forceinline__ float block_max(float x, float* red) {
-  x = wave_max(x);
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  __syncthreads();
-  if (l == 0) red[w] = x;
-  __syncthreads();
-  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-}
-__device__ __forceinline__ float block_sumf(float x, float* red) {
-  x = wave_sumf(x);
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  __syncthreads();
-  if (l == 0) red[w] = x;
-  __syncthreads();
-  return ((red[0] + red[1]) + red[2]) + red[3];
-}
+// Block reduction with a fixed combination order (waves 0..3 in sequence).
 __device__ __forceinline__ double block_sumd(double x, double* red) {
   x = wave_sumd(x);
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
