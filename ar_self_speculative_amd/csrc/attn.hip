@@ -1007,15 +1007,16 @@ constexpr int kDecMergeLoads = 34;  // partials one thread of the in-kernel merg
 
 // The body of the decode kernel. The two LDS buffers arrive as restrict
 // pointers: the compiler then knows that the V copies in flight do not write
-// what phase 1 reads, and phase 1 waits for the K copies only.
-template <int D>
+// what phase 1 reads. LSE32 as in the main kernel: the row sums in fp32 from
+// the unrounded probabilities when the caller wants the log-sum-exp.
+template <int D, bool LSE32>
 __device__ __forceinline__ void attn_dec_body(lds_u8* __restrict__ kb, lds_u8* __restrict__ vb,
                                               float (*__restrict__ rmax)[2][32], float (*__restrict__ rsum)[2][32],
                                               int* __restrict__ last_sh, const int32_t* a_len, const void* a_q,
                                               const void* a_kc, const void* a_vc, int a_R, int a_cap, int a_max_len,
                                               int b, int kvh, int s, int NS, int Hkv, int g, int kdr, int bl,
                                               const AttnParams& p) {
-  using W = Wave<D, 1>;
+  using W = Wave<D, 1, LSE32>;
   using L = Lay<D>;
   constexpr int DSTEPS = D / 16, DT = D / 32;
   const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63;
@@ -1026,10 +1027,10 @@ __device__ __forceinline__ void attn_dec_body(lds_u8* __restrict__ kb, lds_u8* _
   const int RT = (M + 31) / 32;
 
   // The keys of this split: [kbeg, kbeg + nk) of the prefix, or the R step
-  // keys. The K copies go out before the cache length arrives, bounded by the
-  // host's max_len (rows past the length that they bring in are masked before
-  // any use); the V copies wait for the length, since rows past it may hold
-  // anything (NaN included) and P V must never read them.
+  // keys. The K and V copies go out before the cache length arrives, bounded
+  // by the host's max_len. Rows past the length that they bring in may hold
+  // anything (NaN included): their scores are masked before any use, and
+  // their V rows are cleared in LDS before P V reads the tile.
   const uint32_t prb = D * 2, lrb = (uint32_t)Hkv * D * 2;
   const int kbeg = s * kDecChunk;
   const uint16_t* kbase;
@@ -1052,9 +1053,13 @@ __device__ __forceinline__ void attn_dec_body(lds_u8* __restrict__ kb, lds_u8* _
   // Both K tiles and both V tiles are always copied: copies past the
   // resource's end return zeros without touching memory.
   {
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, nk_hint > 0 ? bytes_of(nk_hint) : 0u);
+    const uint32_t nb = nk_hint > 0 ? bytes_of(nk_hint) : 0u;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase, nb);
     copy_tile<D, 4>(rk, vo, 0, rb, kb, wave);
     copy_tile<D, 4>(rk, vo, kBN, rb, kb + L::TILE_BYTES, wave);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, nb);
+    copy_tile<D, 4>(rv, vo, 0, rb, vb, wave);
+    copy_tile<D, 4>(rv, vo, kBN, rb, vb + L::TILE_BYTES, wave);
   }
 
   // phase 1 units of this wave: u = wave and wave + 4, (row tile, key tile) = (u / 2, u % 2)
@@ -1087,11 +1092,6 @@ __device__ __forceinline__ void attn_dec_body(lds_u8* __restrict__ kb, lds_u8* _
   }
   const int nk = __builtin_amdgcn_readfirstlane(local ? a_R : max(0, min(kDecChunk, len - kbeg)));
   const int ntiles = (nk + kBN - 1) / kBN;
-  {
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase, nk > 0 ? bytes_of(nk) : 0u);
-    copy_tile<D, 4>(rv, vo, 0, rb, vb, wave);
-    copy_tile<D, 4>(rv, vo, kBN, rb, vb + L::TILE_BYTES, wave);
-  }
   bool has[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -1101,6 +1101,23 @@ __device__ __forceinline__ void attn_dec_body(lds_u8* __restrict__ kb, lds_u8* _
   const float sl2 = p.scale_log2;
   wait_copies();  // this wave's K and V copies and Q rows have landed
   lds_barrier();  // every K and V tile is in LDS
+
+  // Clear the V rows [nk, ntiles * 64) of the last tile in use: copied from
+  // past the length, they may hold anything, and P V reads whole tiles (a
+  // zero probability times a NaN would still be NaN). Key j of a tile holds
+  // 32 bytes in each column pair, at half j / 32, slot j % 32. Nothing reads
+  // the V tiles before the barriers that follow phase 1. (The step keys'
+  // copies end at the last step key, so their tail arrives as zeros.)
+  if (!local && nk < ntiles * kBN) {
+    constexpr int PIECES = 2 * L::NCP;  // 16-byte pieces per key
+    for (int it = tid; it < (ntiles * kBN - nk) * PIECES; it += 256) {
+      const int key = nk + it / PIECES, pc = it % PIECES;
+      const int kt = key / kBN, j = key % kBN;
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
+          vb + kt * L::TILE_BYTES + (pc >> 1) * kCPS + (j >> 5) * 1024 + (j & 31) * 32 + (pc & 1) * 16) =
+          u32x4{0u, 0u, 0u, 0u};
+    }
+  }
 
   typename W::S sc[2];
 #pragma unroll
@@ -1287,7 +1304,7 @@ __device__ __forceinline__ void attn_dec_body(lds_u8* __restrict__ kb, lds_u8* _
   }
 }
 
-template <int D>
+template <int D, bool LSE32>
 __global__ __launch_bounds__(256, 2) void attn_dec_kernel(
     const int32_t* __restrict__ a_len, const void* __restrict__ a_q, const void* __restrict__ a_kc,
     const void* __restrict__ a_vc, uint32_t a_hkv_g, uint32_t a_k_bl, int a_R, int a_ns, int a_cap,
@@ -1308,7 +1325,7 @@ __global__ __launch_bounds__(256, 2) void attn_dec_kernel(
   w /= NS;
   const int kvh = w % Hkv;
   const int b = w / Hkv;
-  attn_dec_body<D>((lds_u8*)kb, (lds_u8*)vb, rmax, rsum, &last_sh, a_len, a_q, a_kc, a_vc, a_R, a_cap, a_max_len, b,
+  attn_dec_body<D, LSE32>((lds_u8*)kb, (lds_u8*)vb, rmax, rsum, &last_sh, a_len, a_q, a_kc, a_vc, a_R, a_cap, a_max_len, b,
                    kvh, s, NS, Hkv, g, kdr, bl, p);
 }
 
@@ -1445,19 +1462,40 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnParams p) {
 // Split partials of an output row: with RAG (ragged batches), sequence b's
 // splits sit in partial blocks tab[2b] .. tab[2b] + tab[2b+1] - 1 of
 // seq_rows rows each; without, split s of every row is block s of `rows`.
+//
+// Many splits over few rows (the decode regime) would make one thread fold
+// its partials in many dependent rounds of loads. There T = 2^lt adjacent
+// lanes share an output vector instead: lane `sub` takes splits sub,
+// sub + T, ..., all of whose loads (up to CH) go out together, and the T
+// partial merges are combined by xor shuffles in a fixed tree, so results
+// depend only on T, which the host derives from the plan.
+constexpr int kMergeCH = 8;       // splits whose loads one thread has in flight together
+constexpr int kMergeMaxLanes = 16;  // lanes that may share one output vector
+
+// log2 of the lanes sharing an output vector for S splits: the fewest that
+// keep every thread's partial loads in one round (up to kMergeMaxLanes).
+inline int merge_lanes_log2(int S) {
+  int lt = 0;
+  while ((1 << lt) < kMergeMaxLanes && (long)kMergeCH << lt < (long)S) ++lt;
+  return lt;
+}
+
 template <bool BF16, bool RAG>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const void* __restrict__ part_o,
                                                         const float* __restrict__ part_lse, void* __restrict__ out,
                                                         float* __restrict__ lse, uint32_t rows, uint32_t D,
                                                         uint32_t S, const int32_t* __restrict__ tab,
-                                                        uint32_t seq_rows) {
+                                                        uint32_t seq_rows, uint32_t lt) {
   constexpr int VEC = BF16 ? 8 : 4;
-  constexpr int CH = 8;  // splits whose loads are in flight together
-  const uint32_t tpr = D / VEC;  // threads per row
-  // rows * tpr < 2^31 (the output holds fewer than 2^31 elements)
+  constexpr int CH = kMergeCH;
+  const uint32_t tpr = D / VEC;  // output vectors per row
+  const uint32_t T = 1u << lt;
+  // rows * tpr * T < 2^31 (checked by the host)
   const uint32_t gid = __builtin_amdgcn_workgroup_id_x() * 256u + __builtin_amdgcn_workitem_id_x();
-  const uint32_t row = gid / tpr;
-  const uint32_t d = (gid - row * tpr) * VEC;
+  const uint32_t sub = gid & (T - 1), vid = gid >> lt;
+  const uint32_t row = vid / tpr;
+  const uint32_t d = (vid - row * tpr) * VEC;
+  // the T lanes of a vector share its row, so they leave (or stay) together
   if (row >= rows) return;
   uint32_t s_lo = 0, s_n = S;
   size_t stride = rows, pbase = row;
@@ -1473,13 +1511,14 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const void* __restrict_
   float acc[VEC];
 #pragma unroll
   for (int i = 0; i < VEC; ++i) acc[i] = 0.f;
-  for (uint32_t s0 = 0; s0 < s_n; s0 += CH) {
+  for (uint32_t s0 = 0; s0 < s_n; s0 += CH * T) {
     float e[CH];
     float x[CH][VEC];
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      const bool in = s0 + j < s_n;
-      const size_t prow = (size_t)(s_lo + (in ? s0 + j : s0)) * stride + pbase;
+      const uint32_t sj = s0 + j * T + sub;
+      const bool in = sj < s_n;
+      const size_t prow = (size_t)(s_lo + (in ? sj : 0)) * stride + pbase;
       e[j] = in ? part_lse[prow] : kNegInf;
       if (BF16) {
         const uint4 raw = *reinterpret_cast<const uint4*>(reinterpret_cast<const u16*>(part_o) + prow * D + d);
@@ -1517,6 +1556,21 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const void* __restrict_
       for (int i = 0; i < VEC; ++i) acc[i] = fmaf(live ? x[j][i] : 0.f, wgt, acc[i]);
     }
   }
+  // combine the T lanes' merges; lane sub = 0 ends with the whole in a fixed order
+  for (uint32_t o = 1; o < T; o <<= 1) {
+    const float e2 = __shfl_xor(emax, (int)o), w2 = __shfl_xor(wsum, (int)o);
+    float a2[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) a2[i] = __shfl_xor(acc[i], (int)o);
+    const float mx = fmaxf(emax, e2);
+    if (mx == kNegInf) continue;  // neither side has a visible key
+    const float c1 = __builtin_amdgcn_exp2f(emax - mx), c2 = __builtin_amdgcn_exp2f(e2 - mx);
+    wsum = wsum * c1 + w2 * c2;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc[i] = acc[i] * c1 + a2[i] * c2;
+    emax = mx;
+  }
+  if (sub != 0) return;
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
   if (BF16) {
     uint4 pk;
@@ -1537,20 +1591,23 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const void* __restrict_
 
 hipError_t launch_merge(const AttnParams& p, bool bf16, hipStream_t stream) {
   const size_t rows = (size_t)p.B * p.R * p.Hq;
-  const size_t threads = rows * (p.D / (bf16 ? 8 : 4));
+  const int32_t* tab = p.ragged ? p.split_tab : nullptr;
+  // a ragged batch's per-sequence split counts are known on the device only
+  // and stay small; it keeps one lane per output vector
+  const int lt = tab ? 0 : merge_lanes_log2(p.S);
+  const size_t threads = (rows * (p.D / (bf16 ? 8 : 4))) << lt;
   if (threads > 0x7fffffff) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)((threads + 255) / 256);
-  const int32_t* tab = p.ragged ? p.split_tab : nullptr;
   const uint32_t seq_rows = (uint32_t)((size_t)p.R * p.Hq);
   if (bf16 && tab)
     hipLaunchKernelGGL((attn_merge_kernel<true, true>), dim3(grid), dim3(256), 0, stream, p.part_o, p.part_lse, p.out,
-                       p.lse, (uint32_t)rows, (uint32_t)p.D, (uint32_t)p.S, tab, seq_rows);
+                       p.lse, (uint32_t)rows, (uint32_t)p.D, (uint32_t)p.S, tab, seq_rows, (uint32_t)lt);
   else if (bf16)
     hipLaunchKernelGGL((attn_merge_kernel<true, false>), dim3(grid), dim3(256), 0, stream, p.part_o, p.part_lse, p.out,
-                       p.lse, (uint32_t)rows, (uint32_t)p.D, (uint32_t)p.S, tab, seq_rows);
+                       p.lse, (uint32_t)rows, (uint32_t)p.D, (uint32_t)p.S, tab, seq_rows, (uint32_t)lt);
   else
     hipLaunchKernelGGL((attn_merge_kernel<false, false>), dim3(grid), dim3(256), 0, stream, p.part_o, p.part_lse,
-                       p.out, p.lse, (uint32_t)rows, (uint32_t)p.D, (uint32_t)p.S, tab, seq_rows);
+                       p.out, p.lse, (uint32_t)rows, (uint32_t)p.D, (uint32_t)p.S, tab, seq_rows, (uint32_t)lt);
   return hipGetLastError();
 }
 
@@ -1563,24 +1620,30 @@ AttnPlan plan_attn(int dtype, int B, int Hq, int Hkv, int D, int R, int max_len,
   const long M = (long)R * g;
   long base;
   // Decode regime (few packed rows per KV head): a latency-bound kernel that
-  // copies a whole split into LDS at once, selected by TIDAR_ATTN_DECODE=1.
-  // Measured on MI355X it is not faster than the main kernel at these sizes
-  // (both sit near the floor of a launch plus dependent memory round trips),
-  // so the main kernel stays the default. TIDAR_ATTN_FUSED_MERGE=0/1 forces
-  // the merge kernel / the in-kernel merge (the latter within its load bound).
+  // copies a whole 128-key split into LDS at once. On MI355X it beats the
+  // main kernel for up to 32 packed rows per KV head when its workgroups fit
+  // one per CU (256) in one round; past that (e.g. 8 KV heads at 4096
+  // prefix keys: 264 workgroups) and for more rows the main kernel is
+  // faster. TIDAR_ATTN_DECODE=1 selects it wherever it applies (up to 128
+  // rows), =0 never. Its splits are merged by the merge kernel;
+  // TIDAR_ATTN_FUSED_MERGE=1 merges them inside the kernel instead (by the
+  // last-arriving split, within its load bound), which measured slower.
+  const long dec_S = (max_len + kDecChunk - 1) / kDecChunk + 1;  // prefix splits, then the step keys
   const char* dec_env = getenv("TIDAR_ATTN_DECODE");
-  if (dtype == 1 && D == 128 && M <= kDecMaxRows && R <= 128 && forced_splits == 0 && dec_env && atoi(dec_env) == 1) {
+  const bool dec_auto = M <= 32 && (long)B * Hkv * dec_S <= 256;
+  const bool dec_on = dec_env ? atoi(dec_env) == 1 : dec_auto;
+  if (dtype == 1 && D == 128 && M <= kDecMaxRows && R <= 128 && forced_splits == 0 && dec_on) {
     pl.decode = 1;
     pl.nqt = 1;
     pl.waves = 4;
     pl.bm = kBM;
     pl.qtiles = 1;
     pl.chunk = kDecChunk;
-    pl.S = (max_len + kDecChunk - 1) / kDecChunk + 1;  // prefix splits, then the step keys
+    pl.S = (int)dec_S;
     const long items = M * (D / 8);
     const long T = items >= 256 ? 1 : 256 / items;
     const bool fits = (pl.S + T - 1) / T <= kDecMergeLoads;
-    pl.fused_merge = fits && M <= 32;
+    pl.fused_merge = 0;
     if (const char* e = getenv("TIDAR_ATTN_FUSED_MERGE")) pl.fused_merge = fits && atoi(e) != 0;
     pl.counter_bytes = ((size_t)B * Hkv * sizeof(int32_t) + 255) / 256 * 256;
     const size_t prow = (size_t)pl.S * B * R * Hq;
@@ -1637,8 +1700,12 @@ AttnPlan plan_attn(int dtype, int B, int Hq, int Hkv, int D, int R, int max_len,
     //    further rounds;
     //  - the split that owns the last prefix keys also has the step's keys;
     //  - the merge of S > 1 partials costs a fixed part (its launch and the
-    //    kernel boundary), one memory round trip per 8 partials (it folds
-    //    them in rounds of 8) and a part per partial element (~3.3 TB/s).
+    //    kernel boundary), a part that grows by 2500 cycles per 8 splits and
+    //    a part per partial element (~3.3 TB/s). The second term was fitted
+    //    when the merge folded 8 partials per memory round trip; the merge
+    //    now loads up to 128 at once, but a sweep of forced split counts on
+    //    the append-prefill shapes still puts the best counts where this
+    //    term does (it also stands for the costs of more, shorter splits).
     const double F = 16000.0, t1 = 2650.0 * D / 128, t2 = 3300.0 * D / 128;
     const double part_elems = (double)B * R * Hq * D;
     double best = 0.0;
@@ -1689,8 +1756,12 @@ hipError_t launch_attn_bf16(const AttnParams& p, hipStream_t stream) {
       return hipErrorInvalidValue;
     const uint32_t hkv_g = (uint32_t)p.Hkv | ((uint32_t)p.g << 16);
     const uint32_t k_bl = (uint32_t)p.k | ((uint32_t)p.block_len << 16);
-    hipLaunchKernelGGL(attn_dec_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream, p.cache_len, p.q, p.k_cache,
-                       p.v_cache, hkv_g, k_bl, p.R, p.S, p.cap, p.max_len, (int)grid, p);
+    if (p.lse)
+      hipLaunchKernelGGL((attn_dec_kernel<128, true>), dim3((unsigned)grid), dim3(256), 0, stream, p.cache_len, p.q,
+                         p.k_cache, p.v_cache, hkv_g, k_bl, p.R, p.S, p.cap, p.max_len, (int)grid, p);
+    else
+      hipLaunchKernelGGL((attn_dec_kernel<128, false>), dim3((unsigned)grid), dim3(256), 0, stream, p.cache_len, p.q,
+                         p.k_cache, p.v_cache, hkv_g, k_bl, p.R, p.S, p.cap, p.max_len, (int)grid, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.fused_merge) return e;
     return launch_merge(p, true, stream);

@@ -35,18 +35,18 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # on a device copy of known size. Valid only for the attention source it was
 # taken on (sha256 prefix of csrc/attn.hip); any other source reports null.
 ATTN_TRAFFIC = {
-    "30992360c0f7f960": 57132191,
+    "a080370c26f076be": 57156017,
 }
 
 # MFMA utilisation of the main attention kernel at this workload, from a
 # rocprofv3 --pmc pass (SQ_VALU_MFMA_BUSY_CYCLES over 1024 * GRBM_GUI_ACTIVE / 8
 # XCDs), beside the same ratio for the MFMA-only ceiling kernel (a dependent
-# chain of v_mfma_f32_32x32x16_bf16, 97.1%). Keyed like ATTN_TRAFFIC; any other
+# chain of v_mfma_f32_32x32x16_bf16, 96.4%). Keyed like ATTN_TRAFFIC; any other
 # attention source reports null.
 ATTN_COUNTERS = {
-    "30992360c0f7f960": {"mfma_busy_frac": 0.2812, "ceiling_kernel_mfma_busy_frac": 0.9713,
-                         "mfma_busy_frac_of_ceiling": 0.2895, "valu_insts_per_mfma": 5.74,
-                         "mfma_coexec_frac": 0.4338, "wave_cycles_waiting_on_dependencies": 0.3366},
+    "a080370c26f076be": {"mfma_busy_frac": 0.2791, "ceiling_kernel_mfma_busy_frac": 0.9642,
+                         "mfma_busy_frac_of_ceiling": 0.2894, "valu_insts_per_mfma": 5.74,
+                         "mfma_coexec_frac": 0.4349, "wave_cycles_waiting_on_dependencies": 0.3367},
 }
 
 SHAPE = dict(layers=36, batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128, P=4096, k=16,
@@ -519,10 +519,35 @@ def knee_bench(args) -> None:
 
     Hq, Hkv, D = 64, 8, 128
     Ps, Rs = (512, 1024, 2048, 4096), (1, 8, 16, 32, 64, 128, 256, 512)
+    if getattr(args, "knee_rows", ""):
+        Rs = tuple(int(r) for r in args.knee_rows.split(","))
     ceil = knee_ceilings()
     gen = torch.Generator(device="cuda").manual_seed(0)
     nbuf = 32  # distinct caches per timed graph (32 x 16.8 MB at P=4096 > the 256 MB last-level cache)
     table = {}
+    # The floor of one launch in this regime: a plain streaming read of the
+    # prefix K/V bytes (fresh, uncached buffers) in one kernel, and an empty
+    # kernel, each timed as graph nodes like the sweep.
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    floor = {}
+    for P in Ps:
+        nbytes = 2 * Hkv * P * D * 2
+        bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device="cuda") for _ in range(nbuf)]
+
+        def read():
+            for b in bufs:
+                tidar.ceiling("hbm_read", b, 512, sink)
+
+        read()
+        floor[P] = _time_graph(_capture(read), 5) * 1e3 / nbuf
+        del bufs
+
+    def empty():
+        for _ in range(nbuf):
+            tidar.ceiling("empty", 1)
+
+    empty()
+    empty_us = _time_graph(_capture(empty), 5) * 1e3 / nbuf
     for P in Ps:
         kcs = [_rand_bf16((1, Hkv, P + 512, D), gen) for _ in range(nbuf)]
         vcs = [_rand_bf16((1, Hkv, P + 512, D), gen) for _ in range(nbuf)]
@@ -549,8 +574,12 @@ def knee_bench(args) -> None:
     for P in Ps:
         knees[P] = dl.roofline_knee(prefix=P, q_heads=Hq, kv_heads=Hkv, head_dim=D, hbm_gbps=ceil["hbm_read_gbps"],
                                     mfma_tflops=ceil["mfma_bf16_tflops"])
-        f = dl.hinge_fit(Rs, [table[(P, R)] for R in Rs])
-        fits[P] = {key: round(v, 3) for key, v in f.items()}
+        if len(Rs) >= 3:
+            # fitted to the printed (rounded) times, so the record reproduces its own fit
+            f = dl.hinge_fit(Rs, [round(table[(P, R)], 2) for R in Rs])
+            fits[P] = {key: round(v, 3) for key, v in f.items()}
+        else:
+            fits[P] = None  # too few row counts to fit
     k_pick = dl.draft_length(knees[4096], sweep_group=g_sweep, step_group=g_step)
     print(json.dumps({
         "metric": "free-token-slot knee (append-prefill attention, 64 q heads, 8 kv heads, d 128) and draft length",
@@ -559,6 +588,13 @@ def knee_bench(args) -> None:
                    "caches_rotated": nbuf},
         "ceilings": ceil,
         "us": {str(P): [round(table[(P, R)], 2) for R in Rs] for P in Ps},
+        "one_launch_floor": {
+            "kv_read_us": {str(P): round(floor[P], 2) for P in Ps},
+            "empty_kernel_us": round(empty_us, 2),
+            "kv_bytes": {str(P): 2 * Hkv * P * D * 2 for P in Ps},
+            "R1_over_read_floor": {str(P): round(table[(P, 1)] / floor[P], 2) for P in Ps} if 1 in Rs else None,
+            "note": "a single launch streaming the prefix K/V of fresh buffers (512 workgroups) and an empty kernel, "
+                    "graph nodes like the sweep; the sweep's points are two launches (attention and split merge)"},
         "knee_rule": "rows where MFMA time equals HBM time at the measured ceilings (roofline crossing)",
         "knee_rows": {str(P): round(knees[P], 2) for P in Ps},
         "sweep_hinge_fit": {str(P): fits[P] for P in Ps},
@@ -675,6 +711,8 @@ def main():
                     help="only time the sampler (tidar_reject_sample) at batch B, draft length k, vocab V, and exit")
     ap.add_argument("--knee", action="store_true",
                     help="only run the append-prefill sweep, report its knee and the draft length it allows")
+    ap.add_argument("--knee-rows", default="", metavar="R,R,...",
+                    help="with --knee: time only these row counts (e.g. 1 for the decode regime under a tracer)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the hot path is measured on a "

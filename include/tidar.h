@@ -122,12 +122,15 @@ typedef struct {
 } tidar_attn_desc;
 
 /* Workspace bytes tidar_attn_step needs for this descriptor (0 if none).
- * The workspace must be zero-filled before its first use (hipMemset, or
- * torch.zeros): when the decode-regime kernel is selected (environment
- * TIDAR_ATTN_DECODE=1, and few packed query rows per KV head: Hq/Hkv * R <=
- * 128, R <= 128, head_dim 128, bf16, num_splits = 0) its leading bytes hold
- * one arrival counter per (sequence, KV head), which every launch returns to
- * zero. A workspace that only ever serves other launches needs no clearing. */
+ * The decode-regime kernel (bf16, head_dim 128, num_splits = 0, few packed
+ * query rows per KV head) is chosen by itself for Hq/Hkv * R <= 32 when
+ * B * Hkv * (ceil(max_cache_len / 128) + 1) <= 256; environment
+ * TIDAR_ATTN_DECODE=1 selects it up to Hq/Hkv * R <= 128 (R <= 128), =0
+ * never. Its workspace leads with one arrival counter per (sequence, KV
+ * head). They are used only when TIDAR_ATTN_FUSED_MERGE=1 asks it to merge
+ * its splits itself: then the workspace must be zero-filled before its first
+ * use (hipMemset, or torch.zeros), and every launch returns the counters to
+ * zero. Otherwise the workspace needs no clearing. */
 size_t tidar_attn_workspace_bytes(const tidar_attn_desc* desc);
 
 /*

@@ -180,3 +180,26 @@ def test_decode_regime_workspace_layout(monkeypatch):
     f = _desc(num_q_heads=64, num_kv_heads=8, k=1, num_blocks=0, block_len=1, cache_capacity=4104,
               max_cache_len=4096, num_splits=4)
     assert lib.tidar_attn_workspace_bytes(ctypes.byref(f)) == 4 * rows * 128 * 2 + 4 * rows * 4
+
+
+def _is_decode_plan(d, rows):
+    """The decode plan's workspace: counters, then ceil(max_len / 128) + 1 splits."""
+    S = (d.max_cache_len + 127) // 128 + 1
+    counters = (d.batch * d.num_kv_heads * 4 + 255) // 256 * 256
+    return lib.tidar_attn_workspace_bytes(ctypes.byref(d)) == \
+        counters + (S * rows * 128 * 2 + 255) // 256 * 256 + S * rows * 4
+
+
+@pytest.mark.parametrize("P,R,expect", [(512, 1, True), (2048, 1, True), (2048, 4, True),
+                                        (2048, 8, False),    # 64 packed rows per KV head
+                                        (4096, 1, False)])   # 8 x 33 workgroups > 256
+def test_decode_regime_chosen_by_itself(P, R, expect, monkeypatch):
+    """Without the environment switch the decode kernel serves up to 32 packed
+    rows per KV head when its workgroups fit one per CU; otherwise the main
+    kernel's plan stands. TIDAR_ATTN_DECODE=0 turns it off."""
+    monkeypatch.delenv("TIDAR_ATTN_DECODE", raising=False)
+    d = _desc(num_q_heads=64, num_kv_heads=8, k=R, num_blocks=0, block_len=1, cache_capacity=P + 8,
+              max_cache_len=P)
+    assert _is_decode_plan(d, R * 64) == expect
+    monkeypatch.setenv("TIDAR_ATTN_DECODE", "0")
+    assert not _is_decode_plan(d, R * 64)

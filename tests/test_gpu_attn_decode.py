@@ -1,5 +1,6 @@
 """GPU parity of the decode-regime attention kernel (few packed query rows per
-KV head: R * g <= 128, head_dim 128; selected with TIDAR_ATTN_DECODE=1)
+KV head, head_dim 128: chosen by the planner for R * g <= 32 when its
+workgroups fit one per CU, forced up to R * g <= 128 with TIDAR_ATTN_DECODE=1)
 against the fp64 oracle.
 
 The same inputs run three ways: splits merged inside the kernel by the
