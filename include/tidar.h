@@ -140,7 +140,9 @@ size_t tidar_attn_workspace_bytes(const tidar_attn_desc* desc);
  * k_cache  [B, Hkv, cap, D] dtype   this layer's cache. Rows at or past cache_len[b] never
  *                                  affect the result: bf16 k_cache rows below max_cache_len
  *                                  may be loaded (any bit pattern, NaN included, is masked
- *                                  out); v_cache rows at or past cache_len[b] are never read
+ *                                  out); bf16 v_cache rows below max_cache_len may be loaded
+ *                                  by the decode-regime kernel, which clears them before use;
+ *                                  rows at or past max_cache_len are never read
  * v_cache  [B, Hkv, cap, D] dtype
  * cache_len[B] int32        committed prefix length per sequence (device)
  * out      [B, R, Hq, D]    dtype   written
