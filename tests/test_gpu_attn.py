@@ -217,6 +217,37 @@ def test_forced_splits_past_short_sequences_on_a_nan_workspace():
     assert np.abs(lse.cpu().numpy() - rlse).max() <= LSE_TOL["bf16"]
 
 
+@pytest.mark.parametrize("splits", [9, 40, 100, 200])
+def test_many_splits_merge_matches_oracle(splits):
+    """Forced split counts past 8 make the merge spread each output vector's
+    splits over 2, 8 or 16 lanes, all of whose loads go out in one round;
+    200 splits over 16 lanes take two rounds. Prefixes of 12800 keys (200 key
+    tiles, so every count is kept as asked) and 3000 (its later splits hold
+    no keys); every element and log-sum-exp against the oracle, on a
+    workspace filled with NaN bytes first."""
+    import ar_self_speculative_amd as tidar
+    from tests.gpu_util import attn_desc, dev_array, oracle_inputs
+    lens = [12800, 3000]
+    c = attn_case(dtype="bf16", layers=1, batch=2, num_q_heads=8, num_kv_heads=2, head_dim=128, k=1,
+                  num_blocks=2, block_len=1, cache_len=lens, cache_capacity=max(lens) + 8, seed=splits)
+    desc = attn_desc(c, num_splits=splits)
+    rows = c.batch * (c.k + c.num_blocks * c.block_len) * c.num_q_heads
+    assert tidar.attn_workspace_bytes(desc) == (splits * rows * 256 + 255) // 256 * 256 + splits * rows * 4
+    args = [dev_array(c, n, 0) for n in ("q", "k_step", "v_step", "k_cache", "v_cache")]
+    ws = tidar.attn_workspace(desc)
+    ws.fill_(0xFF)
+    out = torch.empty_like(args[0])
+    lse = torch.empty(out.shape[:-1], dtype=torch.float32, device=out.device)
+    tidar.attn_step(desc, *args, torch.from_numpy(c.cache_len).cuda(), out, lse, None, ws)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    ref, rlse = oracle.attn_step(*oracle_inputs(c), c.cache_len, k=c.k, num_blocks=c.num_blocks,
+                                 block_len=c.block_len, sm_scale=c.sm_scale)
+    assert np.isfinite(got).all()
+    assert _report(f"{splits} forced splits, NaN workspace", got, ref, TOL["bf16"]) <= TOL["bf16"]
+    assert np.abs(lse.cpu().numpy() - rlse).max() <= LSE_TOL["bf16"]
+
+
 def _ragged_table(lens, slots, local_tiles, max_len):
     """Host restatement of the device's split apportionment (start, count) per
     sequence: the smallest tiles-per-split c whose counts fit the slots."""
