@@ -150,6 +150,26 @@ def test_config3_one_layer_every_element_at_the_bench_launch():
     assert _report("cfg3 one layer, every element, bench launch", out, ref, TOL["bf16"]) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("lens", [[131072], [131072, 70001]], ids=["one", "ragged"])
+def test_long_prefix_sampled(lens):
+    """A TiDAR step (k = 4, 5 blocks of 4) over a 131072-key prefix (Qwen3-8B
+    heads): alone (the planner's split count over 2048 key tiles, merged by
+    several lanes per output vector) and beside a 70001-key sequence (the
+    ragged apportionment of 64 split slots). Offsets run far into the cache.
+    Sampled rows against the oracle."""
+    c = attn_case(dtype="bf16", layers=1, batch=len(lens), num_q_heads=32, num_kv_heads=8, head_dim=128, k=4,
+                  num_blocks=5, block_len=4, cache_len=lens, cache_capacity=max(lens) + 8, seed=7)
+    out, lse = run_attn(c)
+    rows = _sample_rows(c, 48, seed=5)
+    ref, rlse = oracle.attn_rows(*oracle_inputs(c), c.cache_len, rows, k=c.k, num_blocks=c.num_blocks,
+                                 block_len=c.block_len, sm_scale=c.sm_scale)
+    got = np.stack([out[b, r, h] for b, r, h in rows])
+    assert np.isfinite(out).all()
+    assert _report(f"P={lens}, k=4", got, ref, TOL["bf16"]) <= TOL["bf16"]
+    got_lse = np.array([lse[b, r, h] for b, r, h in rows])
+    assert np.abs(got_lse - rlse).max() <= LSE_TOL["bf16"]
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_long_draft_block_layout_sampled(dtype):
     """k = 64: 64 drafts and 65 blocks of 64 masks (R = 4224 rows), so a query
