@@ -1688,6 +1688,7 @@ AttnPlan plan_attn(int dtype, int B, int Hq, int Hkv, int D, int R, int max_len,
     }
   }
   int S;
+  int bal_ch = 0;  // split size in tiles that counts the step-key tiles into the last split's share (0: none)
   const char* target_env = getenv("TIDAR_ATTN_TARGET_WG");
   if (forced_splits > 0) {
     S = forced_splits;
@@ -1727,6 +1728,15 @@ AttnPlan plan_attn(int dtype, int B, int Hq, int Hkv, int D, int R, int max_len,
         S = se;
       }
     }
+    // Same split count, boundaries moved so that the last split's step-key
+    // tiles count towards its share: ceil((prefix + step-key tiles) / S)
+    // prefix tiles for every split but the last (when that still makes S
+    // splits). With 512 causal rows over 4096 keys, 8 step-key tiles: splits
+    // of 18, 18, 18 and 10 + 8 tiles instead of 16, 16, 16 and 16 + 8.
+    if (ntiles > 0 && local_tiles > 0) {
+      const int ch = (ntiles + local_tiles + S - 1) / S;
+      if ((ntiles + ch - 1) / ch == S) bal_ch = ch;
+    }
   } else {
     // Fill the resident workgroup slots (two per CU on the 256-CU part) in
     // one round: a second, partial round would cost as much as the first.
@@ -1738,7 +1748,7 @@ AttnPlan plan_attn(int dtype, int B, int Hq, int Hkv, int D, int R, int max_len,
     S = std::max(1, std::min(S, std::max(1, ntiles / 2)));
   }
   S = std::max(1, std::min(S, std::max(1, ntiles)));
-  int chunk = ntiles > 0 ? ((ntiles + S - 1) / S) * kBN : kBN;
+  int chunk = ntiles > 0 ? (bal_ch > 0 ? bal_ch : (ntiles + S - 1) / S) * kBN : kBN;
   S = max_len > 0 ? (max_len + chunk - 1) / chunk : 1;
   pl.S = S;
   pl.chunk = chunk;
