@@ -1729,12 +1729,14 @@ AttnPlan plan_attn(int dtype, int B, int Hq, int Hkv, int D, int R, int max_len,
       }
     }
     // Same split count, boundaries moved so that the last split's step-key
-    // tiles count towards its share: ceil((prefix + step-key tiles) / S)
-    // prefix tiles for every split but the last (when that still makes S
-    // splits). With 512 causal rows over 4096 keys, 8 step-key tiles: splits
-    // of 18, 18, 18 and 10 + 8 tiles instead of 16, 16, 16 and 16 + 8.
-    if (ntiles > 0 && local_tiles > 0) {
-      const int ch = (ntiles + local_tiles + S - 1) / S;
+    // tiles count towards its share: ceil((prefix + w * step-key tiles) / S)
+    // prefix tiles for every split but the last, with w = 2 (a step-key tile
+    // goes through the region rule and the masked tile path, and costs about
+    // two prefix tiles), else w = 1, whichever first still makes S splits.
+    // With 512 causal rows over 4096 keys, 8 step-key tiles: splits of 20,
+    // 20, 20 and 4 + 8 tiles instead of 16, 16, 16 and 16 + 8.
+    for (int wl = 2; wl >= 1 && bal_ch == 0 && ntiles > 0 && local_tiles > 0; --wl) {
+      const int ch = (ntiles + wl * local_tiles + S - 1) / S;
       if ((ntiles + ch - 1) / ch == S) bal_ch = ch;
     }
   } else {
