@@ -617,17 +617,20 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
   if (RAG && p.B <= 64) {
     // The sequence and split of slot `slot`: every workgroup shares the S
     // slots out the same way from the clamped lengths. Sequence i weighs
-    // w_i = its prefix tiles plus the step-key tiles of its last split and
-    // takes S_i = max(1, ceil(w_i / c)) slots, c being the smallest tile
-    // count per split with sum S_i <= S (a binary search between
-    // ceil(sum w / S) and ceil(sum w / (S - B)), which always fits); its
-    // splits cover ceil(tiles_i / S_i) tiles each. Lane i holds sequence i.
+    // w_i = its prefix tiles plus twice the step-key tiles of its last split
+    // (a step-key tile goes through the region rule and the masked tile
+    // path, and costs about two prefix tiles) and takes S_i = max(1,
+    // ceil(w_i / c)) slots, c being the smallest weight per split with
+    // sum S_i <= S (a binary search between ceil(sum w / S) and
+    // ceil(sum w / (S - B)), which always fits). Its splits but the last
+    // take ceil(w_i / S_i) prefix tiles each when that still makes S_i
+    // splits, else ceil(tiles_i / S_i). Lane i holds sequence i.
     const int slot = w % S;
     kvh = w / S;
     const int B = p.B, lt = p.local_tiles;
     const int raw_l = lane < B ? a_len[lane] : 0;
     const int li = min(max(raw_l, 0), a_max_len);
-    const int wl = lane < B ? (li + kBN - 1) / kBN + lt : 0;
+    const int wl = lane < B ? (li + kBN - 1) / kBN + 2 * lt : 0;
     const int wsum = __builtin_amdgcn_readfirstlane(wave_sum_int(wl));
     int lo = max(1, (wsum + S - 1) / S), hi = (wsum + (S - B) - 1) / (S - B);
     while (lo < hi) {
@@ -655,7 +658,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
       if (tid == 0 && p.dev_status) atomicOr(p.dev_status, 1);
     }
     len = __builtin_amdgcn_readlane(li, b);
-    chunk = __builtin_amdgcn_readfirstlane(((len + kBN - 1) / kBN + Sb - 1) / Sb * kBN);
+    {  // the last split's step-key tiles count towards its share, as in the weights
+      const int pt = (len + kBN - 1) / kBN, chb = (pt + 2 * lt + Sb - 1) / Sb;
+      chunk = __builtin_amdgcn_readfirstlane(((pt + chb - 1) / max(chb, 1) == Sb ? chb : (pt + Sb - 1) / Sb) * kBN);
+    }
     prow_off = (size_t)(bstart + s - b) * a_R * Hkv * g;
   } else if (RAG) {
     // More than 64 sequences: the same sharing with c = ceil(sum w / (S - B))
@@ -666,7 +672,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
     int wsum = 0;
     for (int i = 0; i < B; ++i) {
       const int li = min(max(a_len[i], 0), a_max_len);
-      wsum += (li + kBN - 1) / kBN + lt;
+      wsum += (li + kBN - 1) / kBN + 2 * lt;
     }
     const int E = S - B;  // > 0 by the plan
     const int c = (wsum + E - 1) / E;
@@ -676,7 +682,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
     Sb = 1;
     for (int i = 0; i < B; ++i) {
       const int li = min(max(a_len[i], 0), a_max_len);
-      const int si = max(1, ((li + kBN - 1) / kBN + lt + c - 1) / c);
+      const int si = max(1, ((li + kBN - 1) / kBN + 2 * lt + c - 1) / c);
       if (writer) {
         p.split_tab[2 * i] = start;
         p.split_tab[2 * i + 1] = si;
@@ -697,7 +703,10 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
       if (tid == 0 && p.dev_status) atomicOr(p.dev_status, 1);
     }
     len = __builtin_amdgcn_readfirstlane(min(max(raw, 0), a_max_len));
-    chunk = __builtin_amdgcn_readfirstlane(((len + kBN - 1) / kBN + Sb - 1) / Sb * kBN);
+    {  // the last split's step-key tiles count towards its share, as in the weights
+      const int pt = (len + kBN - 1) / kBN, chb = (pt + 2 * lt + Sb - 1) / Sb;
+      chunk = __builtin_amdgcn_readfirstlane(((pt + chb - 1) / max(chb, 1) == Sb ? chb : (pt + Sb - 1) / Sb) * kBN);
+    }
     prow_off = (size_t)(bstart + s - b) * a_R * Hkv * g;
   } else {
     s = w % S;

@@ -35,18 +35,18 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # on a device copy of known size. Valid only for the attention source it was
 # taken on (sha256 prefix of csrc/attn.hip); any other source reports null.
 ATTN_TRAFFIC = {
-    "b62ff264961f41d0": 57146537,
+    "05a0a65dff26c701": 57157863,
 }
 
 # MFMA utilisation of the main attention kernel at this workload, from a
 # rocprofv3 --pmc pass (SQ_VALU_MFMA_BUSY_CYCLES over 1024 * GRBM_GUI_ACTIVE / 8
 # XCDs), beside the same ratio for the MFMA-only ceiling kernel (a dependent
-# chain of v_mfma_f32_32x32x16_bf16, 97.3%). Keyed like ATTN_TRAFFIC; any other
+# chain of v_mfma_f32_32x32x16_bf16, 97.2%). Keyed like ATTN_TRAFFIC; any other
 # attention source reports null.
 ATTN_COUNTERS = {
-    "b62ff264961f41d0": {"mfma_busy_frac": 0.2815, "ceiling_kernel_mfma_busy_frac": 0.9726,
-                         "mfma_busy_frac_of_ceiling": 0.2894, "valu_insts_per_mfma": 5.74,
-                         "mfma_coexec_frac": 0.4349, "wave_cycles_waiting_on_dependencies": 0.3377},
+    "05a0a65dff26c701": {"mfma_busy_frac": 0.2819, "ceiling_kernel_mfma_busy_frac": 0.9718,
+                         "mfma_busy_frac_of_ceiling": 0.29, "valu_insts_per_mfma": 5.74,
+                         "mfma_coexec_frac": 0.4344, "wave_cycles_waiting_on_dependencies": 0.3358},
 }
 
 SHAPE = dict(layers=36, batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128, P=4096, k=16,

@@ -98,7 +98,8 @@ int tidar_version(void);
  * is held in the workspace in the input precision (bf16 or fp32), with its
  * log-sum-exp in fp32. With several sequences (batch > 1, bf16, num_splits =
  * 0) the pieces are shared out per sequence on the device, in proportion to
- * each sequence's cache_len, so a ragged batch runs in one round of
+ * each sequence's cache_len plus twice its step keys (a step-key tile costs
+ * about two prefix tiles), so a ragged batch runs in one round of
  * workgroups; the per-sequence split table lives at the start of the
  * workspace and is rewritten by every launch. An optional decode-regime kernel (few packed query
  * rows per KV head, see tidar_attn_workspace_bytes) streams 128-key splits

@@ -270,8 +270,9 @@ def test_many_splits_merge_matches_oracle(splits):
 
 def _ragged_table(lens, slots, local_tiles, max_len):
     """Host restatement of the device's split apportionment (start, count) per
-    sequence: the smallest tiles-per-split c whose counts fit the slots."""
-    w = [(min(max(l, 0), max_len) + 63) // 64 + local_tiles for l in lens]
+    sequence: weights of prefix tiles plus twice the step-key tiles, and the
+    smallest weight per split c whose counts fit the slots."""
+    w = [(min(max(l, 0), max_len) + 63) // 64 + 2 * local_tiles for l in lens]
     count = lambda c: sum(max(1, -(-wi // c)) for wi in w)
     if len(lens) <= 64:
         c = next(c for c in range(1, sum(w) + 1) if count(c) <= slots)
