@@ -58,25 +58,33 @@ __device__ __forceinline__ double wave_sumd(double x) {
   return x;
 }
 
-__device__ __forceinline__ int wave_min_i(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o));
-  return x;
+// Minimum over the wave of per-lane values that grow with the lane index
+// wherever they are set (INT_MAX: not set): the value of the lowest lane that
+// has one, found by ballot rather than a shuffle tree.
+__device__ __forceinline__ int wave_first_i(int x) {
+  const unsigned long long m = __ballot(x != 0x7fffffff);
+  return m ? __builtin_amdgcn_readlane(x, (int)__builtin_ctzll(m)) : 0x7fffffff;
 }
-__device__ __forceinline__ int wave_max_i(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o));
-  return x;
+// Maximum of such values (-1: not set): the value of the highest lane with one.
+__device__ __forceinline__ int wave_last_i(int x) {
+  const unsigned long long m = __ballot(x >= 0);
+  return m ? __builtin_amdgcn_readlane(x, 63 - (int)__builtin_clzll(m)) : -1;
 }
 
-// Block reduction with a fixed combination order (waves 0..3 in sequence).
-__device__ __forceinline__ double block_sumd(double x, double* red) {
+// Two block sums at once, each with a fixed combination order (waves 0..3 in
+// sequence). red holds 8 doubles.
+__device__ __forceinline__ void block_sumd2(double& x, double& y, double* red) {
   x = wave_sumd(x);
+  y = wave_sumd(y);
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   __syncthreads();
-  if (l == 0) red[w] = x;
+  if (l == 0) {
+    red[w] = x;
+    red[4 + w] = y;
+  }
   __syncthreads();
-  return ((red[0] + red[1]) + red[2]) + red[3];
+  x = ((red[0] + red[1]) + red[2]) + red[3];
+  y = ((red[4] + red[5]) + red[6]) + red[7];
 }
 
 __device__ __forceinline__ const float* row_ptr(const RejectParams& p, int b, int rr) {
@@ -331,6 +339,27 @@ __device__ __forceinline__ float2 merge_row_group(const float2* st, int nchunks,
   return make_float2(m, z);
 }
 
+// The same merge with each lane's chunk statistics already in registers
+// (lane j of a group holds chunks j, j + kGroup, ...; chunks past the end
+// and rows past the last hold (-inf, 0)): the same order and arithmetic as
+// merge_row_group, without a round of LDS reads per chunk.
+constexpr int kRegChunks = 8;
+__device__ __forceinline__ float2 merge_row_regs(const float2 (&v)[kRegChunks]) {
+  float m = kNegInf;
+#pragma unroll
+  for (int j = 0; j < kRegChunks; ++j) m = fmaxf(m, v[j].x);
+#pragma unroll
+  for (int o = kGroup / 2; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kGroup));
+  float z = 0.f;
+  if (m != kNegInf)
+#pragma unroll
+    for (int j = 0; j < kRegChunks; ++j)
+      if (v[j].x != kNegInf) z += v[j].y * expf(v[j].x - m);
+#pragma unroll
+  for (int o = kGroup / 2; o > 0; o >>= 1) z += __shfl_xor(z, o, kGroup);
+  return make_float2(m, z);
+}
+
 // Inclusive prefix sum over the block in thread order (fp64); `tot` gets the
 // block total. Uses red[0..3].
 __device__ __forceinline__ double block_scan_incl(double x, double* red, double* tot) {
@@ -394,8 +423,8 @@ __device__ __forceinline__ void pick_token(const RejectParams& p, int b, int k, 
       run += sums[c];
     }
     // one LDS atomic per wave (per-thread atomics on one word serialise)
-    mf = wave_min_i(mf);
-    ml = wave_max_i(ml);
+    mf = wave_first_i(mf);  // thread t's chunks follow thread t - 1's
+    ml = wave_last_i(ml);
     if ((threadIdx.x & 63) == 0) {
       if (mf != 0x7fffffff) atomicMin(&pick_c, mf);
       if (ml >= 0) atomicMax(&last_c, ml);
@@ -452,8 +481,8 @@ __device__ __forceinline__ void pick_token(const RejectParams& p, int b, int k, 
       if (w[j] > 0.f) mine_last = t;
     }
   }
-  mine_first = wave_min_i(mine_first);
-  mine_last = wave_max_i(mine_last);
+  mine_first = wave_first_i(mine_first);  // thread t's tokens follow thread t - 1's
+  mine_last = wave_last_i(mine_last);
   if ((threadIdx.x & 63) == 0) {
     if (mine_first != 0x7fffffff) atomicMin(&first_t, mine_first);
     if (mine_last >= 0) atomicMax(&last_t, mine_last);
@@ -468,10 +497,9 @@ __global__ __launch_bounds__(kThreads) void rej_draw_kernel(const int32_t* __res
                                                              RejectParams p) {
   __shared__ float2 mz[2 * kMaxK + 1];
   __shared__ float2 st_lds[kStage];
-  __shared__ float rho[kMaxK];
-  __shared__ float uni[kMaxK];
-  __shared__ int n_sh, last_sh;
-  __shared__ double redd[4];
+  __shared__ int nw[kMaxK / 64];
+  __shared__ int last_sh;
+  __shared__ double redd[8];
   const int k = (int)(a_k_nch & 0xffff), nch = (int)(a_k_nch >> 16);
   const int c = blockIdx.x % nch, b = blockIdx.x / nch;
   const int nrows = 2 * k + 1;
@@ -481,45 +509,69 @@ __global__ __launch_bounds__(kThreads) void rej_draw_kernel(const int32_t* __res
   // go out together with the statistics below
   const int i = threadIdx.x;
   int d = -1;
-  float da = 0.f, dq = 0.f;
+  float da = 0.f, dq = 0.f, u = 0.f;
   if (i < k) {
     d = a_drafts[(size_t)b * k + i];
-    uni[i] = a_uni[(size_t)b * (k + 1) + i];
+    u = a_uni[(size_t)b * (k + 1) + i];
     da = p.gathered[(size_t)b * 2 * k + i];
     dq = p.gathered[(size_t)b * 2 * k + k + i];
   }
-  // per-row statistics: stage every (row, chunk) pair of this sequence in
-  // LDS with one round of loads, then merge each row across one wave
   const int total = nrows * nch;
-  if (total <= kStage) {
+  const auto put_row = [&](int rr, float2 v) {
+    mz[rr] = v;
+    if (!(isfinite(v.x) && v.y > 0.f && isfinite(v.y)) && c == 0 && p.dev_status) atomicOr(p.dev_status, 8);
+  };
+  // per-row statistics. Up to 64 rows of up to 64 chunks: every lane loads
+  // its two rows' share straight into registers (one round of loads) and
+  // kGroup lanes merge each row.
+  if (nrows <= 2 * (kThreads / kGroup) && nch <= kGroup * kRegChunks) {
     const float2* g = a_stats + (size_t)b * total;
-    float2 v[kStage / kThreads];
+    const int gl = (int)threadIdx.x % kGroup, r0 = (int)threadIdx.x / kGroup, r1 = r0 + kThreads / kGroup;
+    float2 v0[kRegChunks], v1[kRegChunks];
 #pragma unroll
-    for (int j = 0; j < kStage / kThreads; ++j) {
-      const int t = threadIdx.x + kThreads * j;
-      if (t < total) v[j] = g[t];
+    for (int j = 0; j < kRegChunks; ++j) {
+      const int cc = gl + kGroup * j;
+      v0[j] = cc < nch && r0 < nrows ? g[r0 * nch + cc] : make_float2(kNegInf, 0.f);
+      v1[j] = cc < nch && r1 < nrows ? g[r1 * nch + cc] : make_float2(kNegInf, 0.f);
     }
+    const float2 m0 = merge_row_regs(v0), m1 = merge_row_regs(v1);
+    if (gl == 0) {
+      if (r0 < nrows) put_row(r0, m0);
+      if (r1 < nrows) put_row(r1, m1);
+    }
+  } else {
+    // larger shapes: stage every (row, chunk) pair of this sequence in LDS with
+    // one round of loads when they fit, then merge each row across kGroup
+    // lanes; else one wave per row from global memory
+    if (total <= kStage) {
+      const float2* g = a_stats + (size_t)b * total;
+      float2 v[kStage / kThreads];
 #pragma unroll
-    for (int j = 0; j < kStage / kThreads; ++j) {
-      const int t = threadIdx.x + kThreads * j;
-      if (t < total) st_lds[t] = v[j];
+      for (int j = 0; j < kStage / kThreads; ++j) {
+        const int t = threadIdx.x + kThreads * j;
+        if (t < total) v[j] = g[t];
+      }
+#pragma unroll
+      for (int j = 0; j < kStage / kThreads; ++j) {
+        const int t = threadIdx.x + kThreads * j;
+        if (t < total) st_lds[t] = v[j];
+      }
+      __syncthreads();
     }
-    __syncthreads();
-  }
-  // each row merged by a group of kGroup lanes (all rows at once when the
-  // statistics fit in LDS), else by one wave per row from global memory
-  const bool staged = total <= kStage;
-  const int nr_pass = staged ? kThreads / kGroup : kThreads / 64;
-  for (int rr0 = 0; rr0 < nrows; rr0 += nr_pass) {
-    const int rr = rr0 + (staged ? (int)threadIdx.x / kGroup : wave);
-    const float2 v = staged ? merge_row_group(st_lds, p.nchunks, rr, nrows, threadIdx.x % kGroup)
-                            : (rr < nrows ? merge_row_wave(p, b, rr, lane) : make_float2(0.f, 0.f));
-    if (rr < nrows && (staged ? threadIdx.x % kGroup == 0 : lane == 0)) {
-      mz[rr] = v;
-      if (!(isfinite(v.x) && v.y > 0.f && isfinite(v.y)) && c == 0 && p.dev_status) atomicOr(p.dev_status, 8);
+    const bool staged = total <= kStage;
+    const int nr_pass = staged ? kThreads / kGroup : kThreads / 64;
+    for (int rr0 = 0; rr0 < nrows; rr0 += nr_pass) {
+      const int rr = rr0 + (staged ? (int)threadIdx.x / kGroup : wave);
+      const float2 v = staged ? merge_row_group(st_lds, p.nchunks, rr, nrows, threadIdx.x % kGroup)
+                              : (rr < nrows ? merge_row_wave(p, b, rr, lane) : make_float2(0.f, 0.f));
+      if (rr < nrows && (staged ? threadIdx.x % kGroup == 0 : lane == 0)) put_row(rr, v);
     }
   }
   __syncthreads();
+  // thread i < k: the ratio p_i(d) / q_i(d) and whether d_{i+1} is rejected
+  // (u_i >= min(1, ratio)); the accept length n is the first rejection, found
+  // by ballot (k <= 128: waves 0 and 1), or k
+  bool rej = false;
   if (i < k) {
     float r = 0.f;
     if (d < 0 || d >= p.V) {
@@ -530,21 +582,16 @@ __global__ __launch_bounds__(kThreads) void rej_draw_kernel(const int32_t* __res
       const float pq = expf(dq - sq.x) / sq.y;
       r = pq > 0.f ? pa / pq : INFINITY;
     }
-    rho[i] = r;
+    rej = !(u < fminf(1.f, r));
+    if (c == 0 && p.ratio) p.ratio[(size_t)b * k + i] = r;
   }
+  const unsigned long long rb = __ballot(rej);
+  if (wave < kMaxK / 64 && lane == 0) nw[wave] = rb ? wave * 64 + (int)__builtin_ctzll(rb) : k;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int n = 0;
-    while (n < k && uni[n] < fminf(1.f, rho[n])) ++n;
-    n_sh = n;
-  }
-  __syncthreads();
-  const int n = n_sh;
-  if (c == 0) {
-    for (int i = threadIdx.x; i < k; i += kThreads)
-      if (p.ratio) p.ratio[(size_t)b * k + i] = rho[i];
-    if (threadIdx.x == 0) p.accept_len[b] = n;
-  }
+  int n = k;
+#pragma unroll
+  for (int w = 0; w < kMaxK / 64; ++w) n = min(n, nw[w]);
+  if (c == 0 && threadIdx.x == 0) p.accept_len[b] = n;
   DrawRows dr;
   dr.init(p, b, n, mz[n], n < k ? mz[k + 1 + n] : make_float2(0.f, 1.f));
   // per chunk: mass of the draw distribution, and of p_n alone (the
@@ -570,8 +617,7 @@ __global__ __launch_bounds__(kThreads) void rej_draw_kernel(const int32_t* __res
       acc_a += (double)pt;
     }
   }
-  acc = block_sumd(acc, redd);
-  acc_a = block_sumd(acc_a, redd);
+  block_sumd2(acc, acc_a, redd);
   // Publish this chunk's masses; the last of the sequence's workgroups to
   // arrive sees all of them and draws the token. The masses are stored at
   // device scope (written through this XCD's L2), and the arrival count goes
