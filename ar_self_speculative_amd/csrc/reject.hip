@@ -42,19 +42,75 @@ constexpr int kMaxChunks = 1024;
 constexpr int kStage = 4096;            // (row, chunk) statistics staged in LDS per sequence
 constexpr float kNegInf = -INFINITY;
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+// Cross-lane reductions and scans by DPP lane moves (register to register,
+// no trip through the LDS unit as a shuffle takes). dpp<CTRL, ROWS, BANKS>(x,
+// id): each lane's value from the lane that CTRL names; lanes outside the
+// ROWS / BANKS masks, and lanes whose source lies outside their row, get id.
+// CTRL: quad_perm (0x00-0xff), row_shr:n (0x110 + n), row_mirror (0x140),
+// row_half_mirror (0x141), row_bcast:15 (0x142), row_bcast:31 (0x143).
+template <int CTRL, int ROWS = 0xf, int BANKS = 0xf>
+__device__ __forceinline__ float dpp(float x, float id) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(id), __float_as_int(x), CTRL, ROWS, BANKS, false));
+}
+template <int CTRL, int ROWS = 0xf, int BANKS = 0xf>
+__device__ __forceinline__ double dpp(double x, double id) {
+  const long long v = __double_as_longlong(x), w = __double_as_longlong(id);
+  const unsigned lo = (unsigned)__builtin_amdgcn_update_dpp((int)w, (int)v, CTRL, ROWS, BANKS, false);
+  const unsigned hi = (unsigned)__builtin_amdgcn_update_dpp((int)(w >> 32), (int)(v >> 32), CTRL, ROWS, BANKS, false);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+__device__ __forceinline__ float lane63(float x) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63)); }
+__device__ __forceinline__ double lane63(double x) {
+  const long long v = __double_as_longlong(x);
+  const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)v, 63);
+  const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(v >> 32), 63);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+
+// Reduction over each aligned group of 8 lanes, the result in all 8: pairs
+// (xor 1), quads (xor 2), then the two quads (mirror within the 8).
+template <typename T, typename Op>
+__device__ __forceinline__ T group8(T x, T id, Op op) {
+  x = op(x, dpp<0xb1>(x, id));   // quad_perm [1,0,3,2]
+  x = op(x, dpp<0x4e>(x, id));   // quad_perm [2,3,0,1]
+  x = op(x, dpp<0x141>(x, id));  // row_half_mirror
   return x;
 }
-__device__ __forceinline__ float wave_sumf(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+// Reduction over the wave, the result in every lane: groups of 8, rows of 16
+// (mirror), then rows 0+1 into row 1 and 2+3 into row 3 (row_bcast:15), all
+// four into row 3 (row_bcast:31), read from lane 63.
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T x, T id, Op op) {
+  x = group8(x, id, op);
+  x = op(x, dpp<0x140>(x, id));
+  x = op(x, dpp<0x142, 0xa>(x, id));
+  x = op(x, dpp<0x143, 0xc>(x, id));
+  return lane63(x);
 }
-__device__ __forceinline__ double wave_sumd(double x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+struct MaxOp {
+  __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct AddOp {
+  template <typename T>
+  __device__ T operator()(T a, T b) const { return a + b; }
+};
+__device__ __forceinline__ float wave_max(float x) { return wave_reduce(x, kNegInf, MaxOp()); }
+__device__ __forceinline__ float wave_sumf(float x) { return wave_reduce(x, 0.f, AddOp()); }
+__device__ __forceinline__ double wave_sumd(double x) { return wave_reduce(x, 0.0, AddOp()); }
+
+// Inclusive prefix sum over the wave in lane order: within each row of 16 by
+// right shifts of 1, 2, 3 (of the inputs), then 4 and 8 (of the partial
+// sums, into the banks that have such a source), then across rows by the
+// row broadcasts of lanes 15 and 31.
+__device__ __forceinline__ double wave_scan_incl(double x) {
+  const double x0 = x;
+  x += dpp<0x111>(x0, 0.0);
+  x += dpp<0x112>(x0, 0.0);
+  x += dpp<0x113>(x0, 0.0);
+  x += dpp<0x114, 0xf, 0xe>(x, 0.0);
+  x += dpp<0x118, 0xf, 0xc>(x, 0.0);
+  x += dpp<0x142, 0xa>(x, 0.0);
+  x += dpp<0x143, 0xc>(x, 0.0);
   return x;
 }
 
@@ -321,21 +377,19 @@ __device__ __forceinline__ float2 merge_row_wave(const RejectParams& p, int b, i
 // per row, lane j of a group taking chunks j, j + kGroup, ... (a fixed order,
 // so the result is deterministic). Returns the row's (max, sum exp) in the
 // group's lane 0 for row `rr` (rr >= nrows: no row).
-constexpr int kGroup = 8;
+constexpr int kGroup = 8;  // the group8 reduction spans exactly 8 lanes
 __device__ __forceinline__ float2 merge_row_group(const float2* st, int nchunks, int rr, int nrows, int gl) {
   float m = kNegInf;
   if (rr < nrows)
     for (int c = gl; c < nchunks; c += kGroup) m = fmaxf(m, st[rr * nchunks + c].x);
-#pragma unroll
-  for (int o = kGroup / 2; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kGroup));
+  m = group8(m, kNegInf, MaxOp());
   float z = 0.f;
   if (rr < nrows && m != kNegInf)
     for (int c = gl; c < nchunks; c += kGroup) {
       const float2 v = st[rr * nchunks + c];
       if (v.x != kNegInf) z += v.y * expf(v.x - m);
     }
-#pragma unroll
-  for (int o = kGroup / 2; o > 0; o >>= 1) z += __shfl_xor(z, o, kGroup);
+  z = group8(z, 0.f, AddOp());
   return make_float2(m, z);
 }
 
@@ -348,15 +402,13 @@ __device__ __forceinline__ float2 merge_row_regs(const float2 (&v)[kRegChunks]) 
   float m = kNegInf;
 #pragma unroll
   for (int j = 0; j < kRegChunks; ++j) m = fmaxf(m, v[j].x);
-#pragma unroll
-  for (int o = kGroup / 2; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kGroup));
+  m = group8(m, kNegInf, MaxOp());
   float z = 0.f;
   if (m != kNegInf)
 #pragma unroll
     for (int j = 0; j < kRegChunks; ++j)
       if (v[j].x != kNegInf) z += v[j].y * expf(v[j].x - m);
-#pragma unroll
-  for (int o = kGroup / 2; o > 0; o >>= 1) z += __shfl_xor(z, o, kGroup);
+  z = group8(z, 0.f, AddOp());
   return make_float2(m, z);
 }
 
@@ -364,11 +416,7 @@ __device__ __forceinline__ float2 merge_row_regs(const float2 (&v)[kRegChunks]) 
 // block total. Uses red[0..3].
 __device__ __forceinline__ double block_scan_incl(double x, double* red, double* tot) {
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double y = __shfl_up(x, o);
-    if (l >= o) x += y;
-  }
+  x = wave_scan_incl(x);
   __syncthreads();
   if (l == 63) red[w] = x;
   __syncthreads();
