@@ -106,6 +106,20 @@ def test_max_k_and_statistics_past_the_lds_stage():
     assert (ref.accept_len == 128).all()
 
 
+@pytest.mark.parametrize("batch,k,vocab,path", [
+    (2, 31, 262144, "registers, at their limit: 63 rows x 64 chunks"),
+    (8, 40, 8192, "LDS stage: 81 rows"),
+    (2, 8, 300000, "LDS stage: 74 chunks"),
+], ids=["registers-limit", "lds-rows", "lds-chunks"])
+def test_row_statistics_merge_paths(batch, k, vocab, path):
+    """The draw pass merges each row's chunk statistics from registers (up to
+    64 rows of up to 64 chunks), from an LDS stage (up to 4096 pairs), or one
+    wave per row from global memory (the k = 128 test above): every path
+    against the oracle."""
+    case = sampler_case(batch=batch, k=k, vocab=vocab, ar_sigma=2.5, diff_mode="noisy", diff_sigma=0.5, seed=23 + k)
+    compare(case, f"k={k} V={vocab} ({path})")
+
+
 def test_temperature():
     case = sampler_case(batch=128, k=3, vocab=1000, ar_sigma=2.0, diff_mode="noisy", diff_sigma=1.0, seed=11,
                         temperature=0.7)
