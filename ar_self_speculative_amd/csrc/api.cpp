@@ -229,7 +229,6 @@ int tidar_attn_step(const tidar_attn_desc* desc, const void* q, const void* k_st
   p.nqt = plan.nqt;
   p.waves = plan.waves;
   p.decode = plan.decode;
-  p.pp = plan.pp;
   p.fused_merge = plan.fused_merge;
   p.ragged = plan.ragged;
   p.local_tiles = local_tiles_of(desc);

@@ -440,64 +440,6 @@ struct Wave {
     if (NEXT) update_max(mx, sl2);
   }
 
-  // The two phases of step() as separate calls, for a schedule that puts a
-  // workgroup barrier between them. Phase A: this tile's probabilities into
-  // pb (from s_cur) and, with QK, the next tile's scores into s_next. Phase
-  // B: O^T += V^T P^T from pb and, with NEXT, the next tile's maxima and the
-  // reference maximum update. Same instruction order as step().
-  template <bool QK>
-  __device__ __forceinline__ void stepA(const lds_u8* kb_next, const S& s_cur, S& s_next, float sl2, P& pb) {
-    float muse[NQT];
-#pragma unroll
-    for (int nt = 0; nt < NQT; ++nt) muse[nt] = (m[nt] == kNegInf) ? 0.f : m[nt];
-    constexpr int NA = 2 * DSTEPS;
-    bf16x8 kf[NA];
-    if (QK) {
-#pragma unroll
-      for (int nt = 0; nt < NQT; ++nt) s_next[nt][0] = s_next[nt][1] = f32x16{};
-#pragma unroll
-      for (int j = 0; j < LA; ++j) kf[j] = kfrag(kb_next, j >> 1, j & 1);
-    }
-#pragma unroll
-    for (int j = 0; j < NA; ++j) {
-      if (QK && j + LA < NA) kf[j + LA] = kfrag(kb_next, (j + LA) >> 1, (j + LA) & 1);
-      __builtin_amdgcn_sched_barrier(0);
-      if (QK) {
-#pragma unroll
-        for (int nt = 0; nt < NQT; ++nt)
-          s_next[nt][j & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[j], qf[nt][j >> 1], s_next[nt][j & 1], 0, 0, 0);
-      }
-#pragma unroll
-      for (int nt = 0; nt < NQT; ++nt) probs(s_cur, nt, (SPS / 2) * j, SPS / 2, muse[nt], sl2, pb);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-
-  template <bool NEXT>
-  __device__ __forceinline__ void stepB(const lds_u8* vb_cur, const P& pb, const S& s_next, float sl2) {
-    float mx[NQT];
-#pragma unroll
-    for (int nt = 0; nt < NQT; ++nt) mx[nt] = kNegInf;
-    constexpr int NB = 4 * DT;
-    bf16x8 vf[NB];
-#pragma unroll
-    for (int j = 0; j < LB; ++j) vf[j] = vfrag(vb_cur, j / DT, j % DT);
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      if (j + LB < NB) vf[j + LB] = vfrag(vb_cur, (j + LB) / DT, (j + LB) % DT);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int nt = 0; nt < NQT; ++nt)
-        o[nt][j % DT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], pb[nt][j / DT], o[nt][j % DT], 0, 0, 0);
-      if (NEXT && (j % (NB / 4)) == 0) {
-#pragma unroll
-        for (int nt = 0; nt < NQT; ++nt) max8(s_next, nt, j / (NB / 4), mx[nt]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (NEXT) update_max(mx, sl2);
-  }
-
   // max of a whole (masked) tile, then the reference maximum update
   __device__ __forceinline__ void tile_max(const S& s, float sl2) {
     float mx[NQT];
@@ -1042,313 +984,6 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
       const int row = f / CHUNKS, c = f % CHUNKS;
       const uint32_t orow = *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(stage + row * PITCH + 2 * D);
       if (orow == 0xFFFFFFFFu) continue;  // past the last query row
-      const u32x4 val = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(stage + row * PITCH + 16 * c);
-      __builtin_amdgcn_raw_buffer_store_b128(val, orsrc, (int)(orow * (uint32_t)(2 * D) + 16u * (uint32_t)c), 0,
-                                             kStoreDevice);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Paired-item variant of the bf16 kernel: one workgroup of eight waves holds
-// two independent work items (two (sequence, KV head, query tile, split)
-// items of the plan above), waves 0-3 the first and waves 4-7 the second,
-// each with its own Q rows, its own K/V stream and its own LDS tiles. The two
-// run the same tile steps half a step apart: at every workgroup barrier one
-// item enters phase A of a tile step (QK^T of the next tile with the
-// exponentials of this one: VALU-heavy) while the other enters phase B (P V
-// with the next maxima: almost pure MFMA). Each SIMD holds one wave of
-// each item, so its matrix pipe is fed from one phase while the vector unit
-// works for the other, and the shared barrier keeps the two from drifting
-// back into step (with two separate workgroups per CU nothing holds them
-// apart). K[t+2] is copied when phase A of tile t starts and V[t+1] when
-// its phase B starts; each copy has two half-steps to land. Non-ragged
-// launches only; every barrier is executed by all eight waves (the number
-// of half-steps comes from both items' tile counts).
-// ---------------------------------------------------------------------------
-template <int D, bool LSE32, bool PAD>
-__global__ __launch_bounds__(512, 1) void attn_bf16_pp_kernel(
-    const int32_t* __restrict__ a_len, const void* __restrict__ a_q, const void* __restrict__ a_kc, uint32_t a_qt_s,
-    uint32_t a_hkv_g, uint32_t a_k_bl, int a_R, int a_nwg, int a_cap, int a_chunk, int a_max_len, AttnParams p) {
-  using W = Wave<D, 1, LSE32>;
-  using L = Lay<D>;
-  constexpr int DSTEPS = D / 16, DT = D / 32;
-  constexpr int WAVES = 4;        // waves per item
-  constexpr int BM = 32 * WAVES;  // query rows per item
-  constexpr int NPW = L::NLD / WAVES;  // copy instructions per wave per tile
-  __shared__ __attribute__((aligned(1024))) uint8_t tiles[2][4][L::TILE_BYTES];
-  __shared__ int ntot_lds[2];
-
-  const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63;
-  const int wave8 = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = wave8 >> 2, wave = wave8 & 3;
-  const int l32 = lane & 31, half = lane >> 5;
-  lds_u8* const KB[2] = {(lds_u8*)tiles[grp][0], (lds_u8*)tiles[grp][1]};
-  lds_u8* const VB[2] = {(lds_u8*)tiles[grp][2], (lds_u8*)tiles[grp][3]};
-
-  const int qtiles = (int)(a_qt_s & 0xffff), S = (int)(a_qt_s >> 16);
-  const int Hkv = (int)(a_hkv_g & 0xffff), g = (int)(a_hkv_g >> 16);
-  const int kdr = (int)(a_k_bl & 0xffff), bl = (int)(a_k_bl >> 16);
-  const int n_items = p.B * Hkv * qtiles * S;
-  int item = 2 * remap_xcd((int)__builtin_amdgcn_workgroup_id_x(), a_nwg) + grp;
-  const bool has = item < n_items;  // an odd item count leaves the second half of the last workgroup empty
-  if (!has) item = n_items - 1;      // set up a valid item; it computes and stores nothing
-  const int qt = item % qtiles;
-  int w = item / qtiles;
-  const int s = w % S;
-  w /= S;
-  const int kvh = w % Hkv, b = w / Hkv;
-  const int chunk = a_chunk;
-  const size_t prow_off = (size_t)s * p.B * a_R * Hkv * g;
-
-  // as in the single-item kernel: the first prefix K tile's copy goes out
-  // before the cache length arrives, bounded by max_len
-  const bool last = (s == S - 1);
-  const int kbeg = s * chunk;
-  const int nk_hint =
-      __builtin_amdgcn_readfirstlane(max(0, (last ? a_max_len : min(kbeg + chunk, a_max_len)) - kbeg));
-  const size_t head_off = (size_t)(b * Hkv + kvh) * a_cap * D + (size_t)kbeg * D;
-  const uint32_t pvo = copy_voff(lane, D * 2);
-  if (nk_hint > 0)
-    copy_tile<D, WAVES>(make_rsrc(reinterpret_cast<const u16*>(a_kc) + head_off, (uint32_t)nk_hint * (D * 2)), pvo, 0,
-                        D * 2, KB[0], wave);
-
-  const int M = a_R * g;
-  const int Hq = Hkv * g;
-  const bool live = has && (!PAD || qt * BM + wave * 32 < M);
-  W st;
-  st.init_addr(lane);
-  RowRule rules[1];
-  {
-    const int m = qt * BM + wave * 32 + l32;
-    const bool ok = m < M;
-    const int r = ok ? m / g : 0;
-    const int h = kvh * g + (ok ? m - r * g : 0);
-    rules[0] = row_rule(r, kdr, bl);
-    const u16* qp = reinterpret_cast<const u16*>(a_q) + ((size_t)(b * a_R + r) * Hq + h) * D + 8 * half;
-#pragma unroll
-    for (int i = 0; i < DSTEPS; ++i) {
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + 16 * i);
-      st.qf[0][i] = ok ? v : bf16x8{};
-    }
-#pragma unroll
-    for (int i = 0; i < DT; ++i) st.o[0][i] = f32x16{};
-    st.m[0] = kNegInf;
-    st.l[0] = 0.f;
-  }
-
-  int len = __builtin_amdgcn_readfirstlane(a_len[b]);
-  if (len < 0 || len > a_max_len) {
-    if (wave == 0 && lane == 0 && p.dev_status) atomicOr(p.dev_status, 1);
-    len = min(max(len, 0), a_max_len);
-  }
-  const int kend = last ? len : min(kbeg + chunk, len);
-  const int nk = max(0, kend - kbeg);
-  const float sl2 = p.scale_log2;
-
-  TileSeq seq;
-  seq.nk = __builtin_amdgcn_readfirstlane(nk);
-  seq.np = __builtin_amdgcn_readfirstlane((nk + kBN - 1) / kBN);
-  seq.prb = D * 2;
-  seq.pvo = pvo;
-  seq.pk = reinterpret_cast<const u16*>(a_kc) + head_off;
-  seq.pv = reinterpret_cast<const u16*>(p.v_cache) + head_off;
-  seq.pbytes = (uint32_t)nk * seq.prb;
-  seq.nl0 = seq.nl1 = 0;
-  seq.c_lo0 = seq.c_hi0 = seq.c_lo1 = seq.c_hi1 = 0;
-  seq.lrb = (uint32_t)Hkv * D * 2;
-  seq.lvo = copy_voff(lane, seq.lrb);
-  const size_t step_off = ((size_t)b * a_R * Hkv + kvh) * D;
-  seq.lk = reinterpret_cast<const u16*>(p.k_step) + step_off;
-  seq.lv = reinterpret_cast<const u16*>(p.v_step) + step_off;
-  seq.lbytes0 = seq.lbytes1 = 0;
-  if (last) {
-    const int m_lo = qt * BM;
-    const int m_hi = min(M, m_lo + BM) - 1;
-    const LocalRanges lr = local_ranges(m_lo / g, m_hi / g, kdr, bl);
-    const int n = __builtin_amdgcn_readfirstlane(lr.n);
-    if (n > 0) {
-      seq.c_lo0 = __builtin_amdgcn_readfirstlane(lr.a0);
-      seq.c_hi0 = __builtin_amdgcn_readfirstlane(lr.a1);
-      seq.nl0 = __builtin_amdgcn_readfirstlane((seq.c_hi0 - seq.c_lo0 + kBN - 1) / kBN);
-      seq.lbytes0 = (uint32_t)(seq.c_hi0 - 1) * seq.lrb + D * 2;
-    }
-    if (n > 1) {
-      seq.c_lo1 = __builtin_amdgcn_readfirstlane(lr.b0);
-      seq.c_hi1 = __builtin_amdgcn_readfirstlane(lr.b1);
-      seq.nl1 = __builtin_amdgcn_readfirstlane((seq.c_hi1 - seq.c_lo1 + kBN - 1) / kBN);
-      seq.lbytes1 = (uint32_t)(seq.c_hi1 - 1) * seq.lrb + D * 2;
-    }
-  }
-  const int ntot = has ? __builtin_amdgcn_readfirstlane(seq.count()) : 0;
-
-  // ---- prologue: tile 0's scores and maxima; V[0] and K[1] in flight ----
-  typename W::S sA, sB;
-  typename W::P pb;
-  if (ntot > 0 && (nk == 0 || nk_hint == 0)) {
-    // tile 0 is not the first prefix tile: replace what the early copy brought
-    wait_copies();
-    const TileSrc t0 = seq.at(0);
-    copy_tile<D, WAVES>(make_rsrc(t0.k, t0.bytes), t0.vo, t0.row0, t0.row_bytes, KB[0], wave);
-  }
-  if (wave == 0 && lane == 0) ntot_lds[grp] = ntot;
-  wait_copies();
-  __syncthreads();
-  if (ntot > 0) {
-    const TileSrc t0 = seq.at(0);
-    copy_tile<D, WAVES>(make_rsrc(t0.v, t0.bytes), t0.vo, t0.row0, t0.row_bytes, VB[0], wave);
-    if (ntot > 1) {
-      const TileSrc t1 = seq.at(1);
-      copy_tile<D, WAVES>(make_rsrc(t1.k, t1.bytes), t1.vo, t1.row0, t1.row_bytes, KB[1], wave);
-    }
-    if (live) {
-      st.qk(KB[0], sA);
-      if (t0.local)
-        W::template mask<true>(sA, lane, t0.nvalid, t0.c_base, rules);
-      else if (t0.nvalid < kBN)
-        W::template mask<false>(sA, lane, t0.nvalid, 0, rules);
-      st.tile_max(sA, sl2);
-    }
-  }
-  wait_copies();
-  const int nmax = __builtin_amdgcn_readfirstlane(max(ntot_lds[0], ntot_lds[1]));
-
-  // This item's copies at its phase index q (phase A of tile q/2 for even q,
-  // phase B of tile q/2 for odd q). Returns whether any were issued.
-  auto copies = [&](int q) __attribute__((always_inline)) -> bool {
-    const int t = q >> 1;
-    if ((q & 1) == 0) {
-      if (t + 2 >= ntot) return false;
-      const TileSrc a = seq.at(t + 2);
-      copy_tile<D, WAVES>(make_rsrc(a.k, a.bytes), a.vo, a.row0, a.row_bytes, KB[t & 1], wave);
-    } else {
-      if (t + 1 >= ntot) return false;
-      const TileSrc a = seq.at(t + 1);
-      copy_tile<D, WAVES>(make_rsrc(a.v, a.bytes), a.vo, a.row0, a.row_bytes, VB[(t + 1) & 1], wave);
-    }
-    return true;
-  };
-  // end of a half-step: the copies issued in it may stay in flight, the
-  // earlier ones have landed
-  auto settle = [&](bool issued) __attribute__((always_inline)) {
-    if (issued) {
-      static_assert(NPW <= 15, "vmcnt field");
-      __builtin_amdgcn_s_waitcnt(0x0F70 | NPW);  // vmcnt(NPW)
-    } else {
-      wait_copies();
-    }
-  };
-  // tile step t that has a next tile (scores of tile t in sc, of t+1 into sn)
-  auto full_step = [&](int t, typename W::S& sc, typename W::S& sn) __attribute__((always_inline)) {
-    __syncthreads();
-    bool iss = copies(2 * t);
-    st.template stepA<true>(KB[(t + 1) & 1], sc, sn, sl2, pb);
-    const TileSrc n = seq.at(t + 1);
-    if (n.local)
-      W::template mask<true>(sn, lane, n.nvalid, n.c_base, rules);
-    else if (n.nvalid < kBN)
-      W::template mask<false>(sn, lane, n.nvalid, 0, rules);
-    settle(iss);
-    __syncthreads();
-    iss = copies(2 * t + 1);
-    st.template stepB<true>(VB[t & 1], pb, sn, sl2);
-    settle(iss);
-  };
-  // the same barriers and copies, no compute (waves without rows)
-  auto idle_step = [&](int t) __attribute__((always_inline)) {
-    __syncthreads();
-    settle(copies(2 * t));
-    __syncthreads();
-    settle(copies(2 * t + 1));
-  };
-
-  // Half-step h (2 * nmax + 1 of them): the first item is at phase index h,
-  // the second at h - 1 (its first half-step is idle, and the first item's
-  // last one). Tile
-  // steps with a next tile run unrolled by two, so the scores alternate
-  // between sA and sB without copies; the last tile (P V only) is peeled.
-  // The item with fewer tiles pads with barriers, so every wave executes
-  // exactly H of them.
-  if (grp == 1) __syncthreads();
-  const int nfull = max(0, ntot - 1);
-  int t = 0;
-  if (live) {
-    for (; t + 1 < nfull; t += 2) {
-      full_step(t, sA, sB);
-      full_step(t + 1, sB, sA);
-    }
-    if (t < nfull) {
-      full_step(t, sA, sB);
-      sA[0][0] = sB[0][0];
-      sA[0][1] = sB[0][1];
-      ++t;
-    }
-    if (t < ntot) {
-      // no copies are left to issue; V[t] (issued in the previous
-      // half-step) lands before the barrier that precedes its use
-      __syncthreads();
-      st.template stepA<false>(nullptr, sA, sB, sl2, pb);
-      wait_copies();
-      __syncthreads();
-      st.template stepB<false>(VB[t & 1], pb, sB, sl2);
-      ++t;
-    }
-  } else {
-    for (; t < ntot; ++t) idle_step(t);
-  }
-  for (int i = 2 * ntot; i < 2 * nmax; ++i) __syncthreads();
-  if (grp == 0) __syncthreads();
-
-  // ---- epilogue: as in the single-item kernel, per item in its own tiles ----
-  constexpr int PITCH = 2 * D + 16;
-  constexpr int CHUNKS = D / 8;
-  constexpr int PASSES = 32 * CHUNKS / 64;
-  static_assert(32 * PITCH <= L::TILE_BYTES, "staging does not fit");
-  __syncthreads();  // every wave is done with the last tiles
-  {
-    lds_u8* const stage = wave == 0 ? KB[0] : wave == 1 ? KB[1] : wave == 2 ? VB[0] : VB[1];
-    const float ltot = half_sum(st.l[0]);
-    const int m = qt * BM + wave * 32 + l32;
-    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    if (half == 0) {
-      const int r = m / g;
-      const uint32_t orow = (uint32_t)((b * a_R + r) * Hq + kvh * g + (m - r * g));
-      *reinterpret_cast<__attribute__((address_space(3))) uint32_t*>(stage + l32 * PITCH + 2 * D) =
-          (has && m < M) ? orow : 0xFFFFFFFFu;
-    }
-    if (has && m < M && half == 0) {
-      const int r = m / g;
-      const size_t orow = ((size_t)(b * a_R + r) * Hq + kvh * g + (m - r * g));
-      if (S == 1) {
-        if (p.lse) p.lse[orow] = (st.m[0] + log2f(ltot)) * 0.69314718055994531f;
-      } else {
-        const float e = ltot > 0.f ? st.m[0] + log2f(ltot) : kNegInf;
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(e), make_rsrc(p.part_lse + prow_off, 0xFFFFFFFFu),
-                                              (int)(orow * 4u), 0, kStoreDevice);
-      }
-    }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = 32 * dt + 8 * i + 4 * half;
-        bf16x4 v;
-        v[0] = (__bf16)(st.o[0][dt][4 * i + 0] * inv);
-        v[1] = (__bf16)(st.o[0][dt][4 * i + 1] * inv);
-        v[2] = (__bf16)(st.o[0][dt][4 * i + 2] * inv);
-        v[3] = (__bf16)(st.o[0][dt][4 * i + 3] * inv);
-        *reinterpret_cast<__attribute__((address_space(3))) bf16x4*>(stage + l32 * PITCH + 2 * d) = v;
-      }
-    __syncthreads();
-    u16* const obase = S == 1 ? reinterpret_cast<u16*>(p.out) : reinterpret_cast<u16*>(p.part_o) + prow_off * D;
-    const __amdgpu_buffer_rsrc_t orsrc = make_rsrc(obase, 0xFFFFFFFFu);
-#pragma unroll
-    for (int j = 0; j < PASSES; ++j) {
-      const int f = j * 64 + lane;
-      const int row = f / CHUNKS, c = f % CHUNKS;
-      const uint32_t orow =
-          *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>(stage + row * PITCH + 2 * D);
-      if (orow == 0xFFFFFFFFu) continue;
       const u32x4 val = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(stage + row * PITCH + 16 * c);
       __builtin_amdgcn_raw_buffer_store_b128(val, orsrc, (int)(orow * (uint32_t)(2 * D) + 16u * (uint32_t)c), 0,
                                              kStoreDevice);
@@ -2128,11 +1763,6 @@ AttnPlan plan_attn(int dtype, int B, int Hq, int Hkv, int D, int R, int max_len,
   S = max_len > 0 ? (max_len + chunk - 1) / chunk : 1;
   pl.S = S;
   pl.chunk = chunk;
-  // bf16 with four-wave workgroups: TIDAR_ATTN_PP=1 pairs the work items
-  // two to a workgroup, half a tile step apart (attn_bf16_pp_kernel)
-  if (dtype == 1 && pl.waves == 4 && pl.nqt == 1) {
-    if (const char* e = getenv("TIDAR_ATTN_PP")) pl.pp = atoi(e) == 1;
-  }
   // partial outputs in the input precision, then one fp32 log-sum-exp per row
   const size_t prow = (size_t)S * B * R * Hq;
   const size_t elem = dtype == 1 ? 2 : 4;
@@ -2155,40 +1785,6 @@ hipError_t launch_attn_bf16(const AttnParams& p, hipStream_t stream) {
                          p.k_cache, p.v_cache, hkv_g, k_bl, p.R, p.S, p.cap, p.max_len, (int)grid, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.fused_merge) return e;
-    return launch_merge(p, true, stream);
-  }
-  if (p.pp) {
-    const size_t items = (size_t)p.B * p.Hkv * p.qtiles * p.S;
-    const size_t grid = (items + 1) / 2;
-    if (items > 0x7fffffff || p.qtiles > 0xffff || p.S > 0xffff || p.Hkv > 0xffff || p.g > 0xffff ||
-        p.k > 0xffff || p.block_len > 0xffff || p.ragged || p.waves != 4 || p.nqt != 1)
-      return hipErrorInvalidValue;
-    const uint32_t qt_s = (uint32_t)p.qtiles | ((uint32_t)p.S << 16);
-    const uint32_t hkv_g = (uint32_t)p.Hkv | ((uint32_t)p.g << 16);
-    const uint32_t k_bl = (uint32_t)p.k | ((uint32_t)p.block_len << 16);
-    const bool pad = ((size_t)p.R * p.g) % (size_t)kBM != 0;
-#define TIDAR_PP(D_, L_, P_)                                                                                      \
-  hipLaunchKernelGGL((attn_bf16_pp_kernel<D_, L_, P_>), dim3((unsigned)grid), dim3(512), 0, stream, p.cache_len, \
-                     p.q, p.k_cache, qt_s, hkv_g, k_bl, p.R, (int)grid, p.cap, p.chunk, p.max_len, p)
-    const bool l32 = p.lse != nullptr;
-    if (p.D == 128) {
-      if (l32) {
-        if (pad) TIDAR_PP(128, true, true); else TIDAR_PP(128, true, false);
-      } else {
-        if (pad) TIDAR_PP(128, false, true); else TIDAR_PP(128, false, false);
-      }
-    } else if (p.D == 64) {
-      if (l32) {
-        if (pad) TIDAR_PP(64, true, true); else TIDAR_PP(64, true, false);
-      } else {
-        if (pad) TIDAR_PP(64, false, true); else TIDAR_PP(64, false, false);
-      }
-    } else {
-      return hipErrorInvalidValue;
-    }
-#undef TIDAR_PP
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.S == 1) return e;
     return launch_merge(p, true, stream);
   }
   const size_t grid = (size_t)(p.ragged ? 1 : p.B) * p.Hkv * p.qtiles * p.S;

@@ -45,7 +45,6 @@ struct AttnParams {
   int32_t* split_tab;  // [B, 2]
   float sm_scale;
   float scale_log2;  // sm_scale * log2(e)
-  int pp;         // bf16 main path: two work items per 8-wave workgroup, half a tile step apart
 };
 
 struct AttnPlan {
@@ -57,7 +56,6 @@ struct AttnPlan {
   int bm;          // packed query rows per workgroup
   int decode;      // decode-regime kernel: S prefix splits of `chunk` keys plus one split of step keys
   int fused_merge;
-  int pp;          // two work items per 8-wave workgroup (attn_bf16_pp_kernel)
   int ragged;      // split slots apportioned per sequence on the device (S = slots per KV head and query tile)
   size_t ws_bytes;
   size_t counter_bytes;  // leading workspace bytes: arrival counters (decode path) or the split table (ragged)

@@ -76,47 +76,6 @@ def test_workgroup_shape_knob_matches_oracle(waves, monkeypatch):
     assert _report(f"D=64 bf16 waves={waves}", out3, ref3, TOL["bf16"]) <= TOL["bf16"]
 
 
-
-PP_SHAPES = [
-    # (B, lens, k, num_blocks, block_len, Hq, Hkv, D, splits)
-    (1, [4096], 16, 17, 16, 32, 8, 128, 0),   # the Qwen3-8B step's plan (7 splits)
-    (1, [1024], 16, 17, 16, 12, 2, 128, 0),   # Qwen2.5-1.5B layer: 54 items, last query tile half full
-    (1, [300], 16, 17, 16, 4, 1, 128, 3),     # 5 query tiles x 3 splits: an odd item count
-    (2, [65, 700], 4, 5, 4, 8, 2, 128, 0),    # two sequences, one split count (items of unequal length)
-    (1, [0], 4, 5, 4, 4, 1, 128, 0),          # empty prefix: step keys only
-    (1, [129], 12, 0, 1, 8, 8, 128, 1),       # append-prefill rows, one split (output written directly)
-    (1, [333], 16, 17, 16, 8, 1, 64, 0),      # head_dim 64
-    (3, [130, 7, 64], 5, 4, 3, 6, 2, 128, 2),
-]
-
-
-@pytest.mark.parametrize("shape", PP_SHAPES, ids=lambda s: f"B{s[0]}-P{max(s[1])}-k{s[2]}-g{s[5] // s[6]}-D{s[7]}-S{s[8]}")
-@pytest.mark.parametrize("with_lse", [False, True])
-def test_paired_items_kernel_matches_oracle_and_single_item_kernel(shape, with_lse, monkeypatch):
-    """TIDAR_ATTN_PP=1: two work items per 8-wave workgroup, half a tile step
-    apart. Every item runs the same instructions in the same order as in the
-    four-wave kernel, so the output (and LSE) must equal that kernel's bit
-    for bit, and the oracle's within tolerance. Several sequences are run
-    with one split count (TIDAR_ATTN_RAGGED=0), the paired kernel's only
-    multi-sequence mode."""
-    B, lens, k, nb, bl, Hq, Hkv, D, splits = shape
-    monkeypatch.setenv("TIDAR_ATTN_DECODE", "0")
-    monkeypatch.setenv("TIDAR_ATTN_RAGGED", "0")
-    cap = max(lens) + k + 5
-    c = attn_case(dtype="bf16", layers=1, batch=B, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, k=k,
-                  num_blocks=nb, block_len=bl, cache_len=lens, cache_capacity=cap, seed=sum(lens) + 3 * k)
-    monkeypatch.setenv("TIDAR_ATTN_PP", "0")
-    base, base_lse = run_attn(c, num_splits=splits, with_lse=with_lse)
-    monkeypatch.setenv("TIDAR_ATTN_PP", "1")
-    out, lse = run_attn(c, num_splits=splits, with_lse=with_lse)
-    ref, rlse = _oracle_full(c)
-    assert np.isfinite(out).all()
-    assert _report(f"paired items {shape} lse={with_lse}", out, ref, TOL["bf16"]) <= TOL["bf16"]
-    assert np.array_equal(out, base)  # bf16 values widened exactly: equal means bit for bit
-    if with_lse:
-        assert np.abs(lse - rlse).max() <= LSE_TOL["bf16"]
-        assert np.array_equal(lse, base_lse)
-
 SMALL = [
     # (B, lens, k, num_blocks, block_len, Hq, Hkv, D)
     (1, [0], 4, 5, 4, 4, 1, 128),            # empty prefix: local keys only
