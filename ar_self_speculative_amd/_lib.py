@@ -40,7 +40,7 @@ EXPORTS = (
     "tidar_logprob_workspace_bytes", "tidar_token_logprobs",
     # measurement kernels (include/tidar_ceilings.h)
     "tidar_ceiling_hbm_read", "tidar_ceiling_mfma_bf16", "tidar_ceiling_exp_f32", "tidar_ceiling_fma_f32",
-    "tidar_ceiling_lds_read_b128", "tidar_ceiling_lds_read_tr16", "tidar_ceiling_empty",
+    "tidar_ceiling_lds_read_b128", "tidar_ceiling_lds_read_tr16", "tidar_ceiling_empty", "tidar_attn_stamps",
 )
 
 
@@ -100,6 +100,8 @@ def load() -> ctypes.CDLL:
         getattr(lib, name).argtypes = [ctypes.c_int, ctypes.c_int, vp, vp]
     lib.tidar_ceiling_empty.restype = ctypes.c_int
     lib.tidar_ceiling_empty.argtypes = [ctypes.c_int, vp]
+    lib.tidar_attn_stamps.restype = ctypes.c_int
+    lib.tidar_attn_stamps.argtypes = [vp, ctypes.c_int]
     return lib
 
 
@@ -284,3 +286,15 @@ def ceiling(name: str, *args, stream=None):
         rc = getattr(_lib, "tidar_ceiling_" + name)(int(grid), int(iters), _ptr(sink), st)
     if rc != 0:
         raise RuntimeError(f"tidar_ceiling_{name} returned {rc}")
+
+
+def attn_stamps(max_workgroups: int):
+    """The per-workgroup records of the last attention launch made with
+    TIDAR_ATTN_STAMPS=1 (include/tidar_ceilings.h): a [max_workgroups, 8]
+    uint64 numpy array."""
+    import numpy as np
+    out = np.zeros((max_workgroups, 8), dtype=np.uint64)
+    rc = _lib.tidar_attn_stamps(out.ctypes.data, int(max_workgroups))
+    if rc != 0:
+        raise RuntimeError(f"tidar_attn_stamps returned {rc}")
+    return out

@@ -9,6 +9,7 @@
 #include <string>
 
 #include "tidar.h"
+#include "tidar_ceilings.h"
 #include "tidar_internal.h"
 
 namespace {
@@ -177,6 +178,11 @@ const char* tidar_last_error(void) { return g_err.c_str(); }
 
 int tidar_version(void) { return 100; }
 
+int tidar_attn_stamps(uint64_t* dst, int max_workgroups) {
+  if (!dst || max_workgroups < 0) return -1;
+  return tidar::read_attn_stamps(reinterpret_cast<unsigned long long*>(dst), max_workgroups) == hipSuccess ? 0 : -5;
+}
+
 size_t tidar_attn_workspace_bytes(const tidar_attn_desc* desc) {
   tidar::AttnPlan plan;
   if (check_desc(desc, &plan) != TIDAR_OK) return 0;
@@ -231,6 +237,7 @@ int tidar_attn_step(const tidar_attn_desc* desc, const void* q, const void* k_st
   p.decode = plan.decode;
   p.fused_merge = plan.fused_merge;
   p.ragged = plan.ragged;
+  p.stamps = plan.stamps;
   p.local_tiles = local_tiles_of(desc);
   p.sm_scale = desc->sm_scale;
   p.scale_log2 = desc->sm_scale * 1.4426950408889634f;

@@ -582,10 +582,24 @@ __device__ __forceinline__ void tile_iter(Wave<D, NQT, LSE32>& st, lds_u8* __res
 // RAG: ragged batch (split slots apportioned per sequence); PAD: the last
 // query tile is only partly filled. Template parameters, so that launches
 // without them carry none of their code.
-template <int D, int NQT, int WAVES, bool LSE32, bool RAG, bool PAD>
+// Per-workgroup timestamps of the STAMP instantiation (a measurement build
+// of the launch that computes exactly what the plain one does; only the
+// 128-dim, four-wave, non-ragged launch without LSE has it): wave 0 of
+// workgroup w writes record w of kStampFields 64-bit words.
+constexpr int kStampFields = 8;
+constexpr int kStampMaxWG = 4096;
+__device__ unsigned long long g_attn_stamps[kStampMaxWG * kStampFields];
+
+template <int D, int NQT, int WAVES, bool LSE32, bool RAG, bool PAD, bool STAMP = false>
 __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kernel(
     const int32_t* __restrict__ a_len, const void* __restrict__ a_q, const void* __restrict__ a_kc, uint32_t a_qt_s,
     uint32_t a_hkv_g, uint32_t a_k_bl, int a_R, int a_nwg, int a_cap, int a_chunk, int a_max_len, AttnParams p) {
+  // shader-clock counter and the 100 MHz reference at entry
+  unsigned long long st_entry = 0, st_rentry = 0, st_pro = 0, st_loop = 0;
+  if (STAMP) {
+    st_entry = __builtin_amdgcn_s_memtime();
+    st_rentry = __builtin_amdgcn_s_memrealtime();
+  }
   using W = Wave<D, NQT, LSE32>;
   using L = Lay<D>;
   constexpr int DSTEPS = D / 16, DT = D / 32;
@@ -875,6 +889,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
     wait_copies();
   }
   if (ntot == 0) wait_copies();  // the early copy lands before KB[0] is reused for staging
+  if (STAMP) st_pro = __builtin_amdgcn_s_memtime();  // tile 0's scores and maxima are in registers
   // iterations whose next tile is a full prefix tile run a loop of their own
   const int tmain = __builtin_amdgcn_readfirstlane(max(0, min(nk / kBN, ntot) - 1));
   // Unrolled by two: the scores of the current tile alternate between sA
@@ -918,6 +933,7 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
     if (live) st.template step<false, false>(nullptr, (t & 1) ? VB[1] : VB[0], sA, sB, sl2);
   }
 
+  if (STAMP) st_loop = __builtin_amdgcn_s_memtime();  // this wave's last tile is done
   // o[nt][dt][v] holds O^T[d = 32*dt + 8*(v/4) + 4*half + v%4][this lane's row].
   // Each 32-row group is normalised, rounded to bf16 and staged row-major in
   // LDS (row pitch 2*D + 16 bytes; the row's output index sits in the
@@ -987,6 +1003,27 @@ __global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1) void attn_bf16_kern
       const u32x4 val = *reinterpret_cast<const __attribute__((address_space(3))) u32x4*>(stage + row * PITCH + 16 * c);
       __builtin_amdgcn_raw_buffer_store_b128(val, orsrc, (int)(orow * (uint32_t)(2 * D) + 16u * (uint32_t)c), 0,
                                              kStoreDevice);
+    }
+  }
+  if (STAMP) {
+    // end: this wave's stores acknowledged
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    const unsigned long long st_end = __builtin_amdgcn_s_memtime();
+    const unsigned long long st_rend = __builtin_amdgcn_s_memrealtime();
+    const int wg = (int)__builtin_amdgcn_workgroup_id_x();
+    if (wave == 0 && lane == 0 && wg < kStampMaxWG) {
+      const unsigned hw = __builtin_amdgcn_s_getreg(0xF804);   // HW_ID: wave, SIMD, CU, SA, SE
+      const unsigned xcc = __builtin_amdgcn_s_getreg(0xF814);  // XCC_ID
+      unsigned long long* r = g_attn_stamps + (size_t)wg * kStampFields;
+      r[0] = st_entry;
+      r[1] = st_rentry;
+      r[2] = st_pro;
+      r[3] = st_loop;
+      r[4] = st_end;
+      r[5] = st_rend;
+      r[6] = (unsigned long long)hw | ((unsigned long long)xcc << 32);
+      r[7] = (unsigned long long)(unsigned)ntot | ((unsigned long long)(unsigned)s << 16) |
+             ((unsigned long long)(unsigned)a_nwg << 32);
     }
   }
 }
@@ -1763,6 +1800,8 @@ AttnPlan plan_attn(int dtype, int B, int Hq, int Hkv, int D, int R, int max_len,
   S = max_len > 0 ? (max_len + chunk - 1) / chunk : 1;
   pl.S = S;
   pl.chunk = chunk;
+  // TIDAR_ATTN_STAMPS=1: the timestamped instantiation where it exists
+  if (const char* e = getenv("TIDAR_ATTN_STAMPS")) pl.stamps = dtype == 1 && atoi(e) == 1;
   // partial outputs in the input precision, then one fp32 log-sum-exp per row
   const size_t prow = (size_t)S * B * R * Hq;
   const size_t elem = dtype == 1 ? 2 : 4;
@@ -1818,7 +1857,10 @@ hipError_t launch_attn_bf16(const AttnParams& p, hipStream_t stream) {
   } while (0)
   // packed query rows that leave the last tile (32 rows per wave) partly empty
   const bool pad = ((size_t)p.R * p.g) % (size_t)(32 * p.waves * p.nqt) != 0;
-  if (p.D == 128 && p.waves == 8) {
+  if (p.stamps && p.D == 128 && p.waves == 4 && !l32 && !p.ragged && !pad && grid <= (size_t)kStampMaxWG) {
+    hipLaunchKernelGGL((attn_bf16_kernel<128, 1, 4, false, false, false, true>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, TIDAR_ATTN_ARGS);
+  } else if (p.D == 128 && p.waves == 8) {
     if (l32) TIDAR_LAUNCH(128, 8, true); else TIDAR_LAUNCH(128, 8, false);
   } else if (p.D == 128 && p.waves == 4) {
     if (l32) TIDAR_LAUNCH(128, 4, true); else TIDAR_LAUNCH(128, 4, false);
@@ -1834,6 +1876,13 @@ hipError_t launch_attn_bf16(const AttnParams& p, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.S == 1) return e;
   return launch_merge(p, true, stream);
+}
+
+hipError_t read_attn_stamps(unsigned long long* host_dst, int max_workgroups) {
+  const int n = std::min(std::max(max_workgroups, 0), kStampMaxWG);
+  if (n == 0) return hipSuccess;
+  return hipMemcpyFromSymbol(host_dst, HIP_SYMBOL(g_attn_stamps), (size_t)n * kStampFields * sizeof(unsigned long long),
+                             0, hipMemcpyDeviceToHost);
 }
 
 hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream) {

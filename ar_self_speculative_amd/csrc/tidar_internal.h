@@ -45,6 +45,7 @@ struct AttnParams {
   int32_t* split_tab;  // [B, 2]
   float sm_scale;
   float scale_log2;  // sm_scale * log2(e)
+  int stamps;        // the timestamped instantiation of the bf16 kernel (measurement)
 };
 
 struct AttnPlan {
@@ -57,6 +58,7 @@ struct AttnPlan {
   int decode;      // decode-regime kernel: S prefix splits of `chunk` keys plus one split of step keys
   int fused_merge;
   int ragged;      // split slots apportioned per sequence on the device (S = slots per KV head and query tile)
+  int stamps;      // TIDAR_ATTN_STAMPS=1: per-workgroup timestamps (measurement build of the same launch)
   size_t ws_bytes;
   size_t counter_bytes;  // leading workspace bytes: arrival counters (decode path) or the split table (ragged)
 };
@@ -65,6 +67,8 @@ AttnPlan plan_attn(int dtype, int B, int Hq, int Hkv, int D, int R, int max_len,
                    int local_tiles);
 hipError_t launch_attn_bf16(const AttnParams& p, hipStream_t stream);
 hipError_t launch_attn_f32(const AttnParams& p, hipStream_t stream);
+// copies the per-workgroup records of the last timestamped attention launch
+hipError_t read_attn_stamps(unsigned long long* host_dst, int max_workgroups);
 
 struct CommitParams {
   int L, B, Hkv, D, k, step_rows, cap, elem_bytes;

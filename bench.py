@@ -35,18 +35,18 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # on a device copy of known size. Valid only for the attention source it was
 # taken on (sha256 prefix of csrc/attn.hip); any other source reports null.
 ATTN_TRAFFIC = {
-    "05a0a65dff26c701": 57157863,
+    "9f896ed05fd7059d": 57159857,
 }
 
 # MFMA utilisation of the main attention kernel at this workload, from a
 # rocprofv3 --pmc pass (SQ_VALU_MFMA_BUSY_CYCLES over 1024 * GRBM_GUI_ACTIVE / 8
 # XCDs), beside the same ratio for the MFMA-only ceiling kernel (a dependent
-# chain of v_mfma_f32_32x32x16_bf16, 97.2%). Keyed like ATTN_TRAFFIC; any other
+# chain of v_mfma_f32_32x32x16_bf16, 96.7%). Keyed like ATTN_TRAFFIC; any other
 # attention source reports null.
 ATTN_COUNTERS = {
-    "05a0a65dff26c701": {"mfma_busy_frac": 0.2819, "ceiling_kernel_mfma_busy_frac": 0.9718,
-                         "mfma_busy_frac_of_ceiling": 0.29, "valu_insts_per_mfma": 5.74,
-                         "mfma_coexec_frac": 0.4344, "wave_cycles_waiting_on_dependencies": 0.3358},
+    "9f896ed05fd7059d": {"mfma_busy_frac": 0.2807, "ceiling_kernel_mfma_busy_frac": 0.9665,
+                         "mfma_busy_frac_of_ceiling": 0.2904, "valu_insts_per_mfma": 5.74,
+                         "mfma_coexec_frac": 0.4337, "wave_cycles_waiting_on_dependencies": 0.3364},
 }
 
 SHAPE = dict(layers=36, batch=1, num_q_heads=32, num_kv_heads=8, head_dim=128, P=4096, k=16,
@@ -499,6 +499,74 @@ def knee_ceilings() -> dict:
     return {"hbm_read_gbps": round(hbm, 1), "mfma_bf16_tflops": round(mfma, 1)}
 
 
+def stamps_bench(args) -> None:
+    """Where one attention launch of the headline step spends its time: the
+    timestamped instantiation of the main kernel (TIDAR_ATTN_STAMPS=1, the
+    same computation with per-workgroup s_memtime / s_memrealtime records)
+    launched eagerly --steps times on layer 0; medians over the launches."""
+    import torch
+
+    import ar_self_speculative_amd as tidar
+    from tidar_synth import fill_device_step
+
+    s = SHAPE
+    torch.cuda.set_device(0)
+    step = tidar.DecodeStep(layers=1, batch=s["batch"], num_q_heads=s["num_q_heads"],
+                            num_kv_heads=s["num_kv_heads"], head_dim=s["head_dim"], k=s["k"],
+                            cache_capacity=s["P"] + s["k"], max_cache_len=s["P"], vocab=s["vocab"])
+    fill_device_step(step, seed=0, cache_len=s["P"])
+    os.environ.pop("TIDAR_ATTN_STAMPS", None)
+    step.attention(0)
+    torch.cuda.synchronize()
+    plain = step.out[0].clone()
+    os.environ["TIDAR_ATTN_STAMPS"] = "1"
+    per = []
+    try:
+        for _ in range(max(1, args.steps)):
+            step.out.zero_()
+            step.attention(0)
+            torch.cuda.synchronize()
+            r = tidar.attn_stamps(4096).astype(np.int64)
+            nwg = int(r[0, 7] >> 32)
+            if nwg <= 0 or nwg > 4096:
+                print("no timestamped launch (the plan did not select it)", file=sys.stderr)
+                sys.exit(1)
+            r = r[:nwg]
+            same = bool(torch.equal(step.out[0], plain))
+            ghz = (r[:, 4] - r[:, 0]) / ((r[:, 5] - r[:, 1]) * 10.0)       # cycles per ns
+            us = lambda cyc: cyc / ghz / 1e3                              # noqa: E731
+            rt0, rt1 = r[:, 1], r[:, 5]
+            xcc = (r[:, 6] >> 32) & 0xF
+            xcc_start = [float((rt0[xcc == x].min() - rt0.min()) / 100.0) for x in range(8) if np.any(xcc == x)]
+            per.append({
+                "span_us": float((rt1.max() - rt0.min()) / 100.0),
+                "last_start_after_first_us": float((rt0.max() - rt0.min()) / 100.0),
+                "prologue_us_median": float(np.median(us(r[:, 2] - r[:, 0]))),
+                "loop_us_median": float(np.median(us(r[:, 3] - r[:, 2]))),
+                "epilogue_us_median": float(np.median(us(r[:, 4] - r[:, 3]))),
+                "slowest_end_after_median_us": float((rt1.max() - np.median(rt1)) / 100.0),
+                "shader_clock_ghz_median": float(np.median(ghz)),
+                "xcd_first_start_us": xcc_start,
+                "output_bitwise_equal_to_plain_launch": same,
+                "workgroups": nwg,
+                "tiles_per_workgroup": sorted(set(int(v) for v in (r[:, 7] & 0xFFFF))),
+            })
+    finally:
+        os.environ.pop("TIDAR_ATTN_STAMPS", None)
+    keys = [k for k, v in per[0].items() if isinstance(v, float)]
+    med = {k: round(float(np.median([p[k] for p in per])), 3) for k in keys}
+    print(json.dumps({
+        "metric": "attention launch breakdown (timestamped main kernel)", "unit": "us", "n_gpus": 1,
+        "data": "synthetic", "dtype": "bf16",
+        "config": {"workload": "one Qwen3-8B-shaped layer of the decode step, P=4096, k=16, library plan",
+                   "launches": len(per)},
+        "median_over_launches": med,
+        "output_bitwise_equal_to_plain_launch": all(p["output_bitwise_equal_to_plain_launch"] for p in per),
+        "workgroups": per[0]["workgroups"], "tiles_per_workgroup": per[0]["tiles_per_workgroup"],
+        "xcd_first_start_us_first_launch": [round(v, 3) for v in per[0]["xcd_first_start_us"]],
+    }), flush=True)
+
+
 def knee_bench(args) -> None:
     """Free-token-slot knee and the draft length it gives.
 
@@ -709,6 +777,8 @@ def main():
                     help="only measure the machine ceilings (HBM read, MFMA, exp/FMA rates, empty kernel) and exit")
     ap.add_argument("--sampler", default="", metavar="B:k[:V]",
                     help="only time the sampler (tidar_reject_sample) at batch B, draft length k, vocab V, and exit")
+    ap.add_argument("--stamps", action="store_true",
+                    help="per-workgroup timestamps of one attention launch (timestamped main kernel)")
     ap.add_argument("--knee", action="store_true",
                     help="only run the append-prefill sweep, report its knee and the draft length it allows")
     ap.add_argument("--knee-rows", default="", metavar="R,R,...",
@@ -734,6 +804,9 @@ def main():
         return
     if args.sampler:
         sampler_bench(args)
+        return
+    if args.stamps:
+        stamps_bench(args)
         return
     if args.knee:
         knee_bench(args)
@@ -790,6 +863,16 @@ def main():
     if status:
         print(f"device status flags set: {status}", file=sys.stderr)
         sys.exit(1)
+    # what the timed step decided: every replay verifies the same synthetic
+    # drafts with the same uniforms, so it is one accept length (the
+    # ragged-batch mode, --config5, reports the distribution over chained
+    # steps); acceptance tests within 1e-5 of their threshold among those
+    # the chain consulted, by the GPU's own ratios
+    acc_n = int(step.accept_len[0].item())
+    u0 = step.uniforms[0].float().cpu().numpy()
+    r0 = step.ratio[0].float().cpu().numpy()
+    tested = np.arange(min(acc_n + 1, s["k"]))
+    near = int(np.sum(np.abs(u0[tested] - np.minimum(1.0, r0[tested])) < 1e-5))
 
     cnt = algorithmic_counts(s["layers"], s["batch"], s["num_q_heads"], s["num_kv_heads"], s["head_dim"],
                              s["P"], s["k"], s["vocab"])
@@ -823,6 +906,8 @@ def main():
         "compulsory_frac_of_hbm_peak": round(comp_bytes / t_step / 1e9 / HBM_PEAK_GBPS, 4),
         "kv_read_frac_of_hbm_peak": round(kv_gbps / HBM_PEAK_GBPS, 4),
         "attn_us_per_layer": round(attn_ms * 1e3, 2),
+        "sampler": {"accept_len": acc_n, "tokens_per_step": acc_n + 1, "accept_near_ties": near,
+                    "inputs": "one synthetic set (diffusion = AR + N(0,1) noise) replayed every step"},
         "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel<128> (+ split merge)",
                      "achieved": round(achieved_tflops, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved_tflops / BF16_MFMA_PEAK_TFLOPS, 4),

@@ -48,6 +48,21 @@ int tidar_ceiling_fma_f32(int grid, int iters, float* sink, void* stream);
  * boundary cost). */
 int tidar_ceiling_empty(int grid, void* stream);
 
+/* Per-workgroup timestamps of the last attention launch made with the
+ * environment variable TIDAR_ATTN_STAMPS=1 set when tidar_attn_step was
+ * called (it selects a timestamped instantiation of the bf16 main kernel
+ * that computes exactly what the plain one does; only the head_dim-128,
+ * single-sequence-plan launch without an LSE output has one, other launches
+ * run unstamped). Copies the records of the first `max_workgroups`
+ * workgroups (at most 4096) into host memory `dst`, 8 uint64 each:
+ * shader-clock counter (s_memtime) at entry, the 100 MHz reference
+ * (s_memrealtime) at entry, s_memtime once tile 0's scores are in registers,
+ * s_memtime after the tile loop, s_memtime and s_memrealtime after the
+ * output stores are acknowledged, HW_ID | XCC_ID << 32, and tiles | split
+ * << 16 | grid size << 32. Synchronous: waits for the device copy. Returns
+ * 0, -1 for a bad argument, -5 when the copy fails. */
+int tidar_attn_stamps(uint64_t* dst, int max_workgroups);
+
 #ifdef __cplusplus
 }
 #endif

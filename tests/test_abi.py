@@ -203,3 +203,10 @@ def test_decode_regime_chosen_by_itself(P, R, expect, monkeypatch):
     assert _is_decode_plan(d, R * 64) == expect
     monkeypatch.setenv("TIDAR_ATTN_DECODE", "0")
     assert not _is_decode_plan(d, R * 64)
+
+
+def test_attn_stamps_rejects_bad_arguments():
+    """The timestamp reader checks its arguments on the host before any copy."""
+    assert lib.tidar_attn_stamps(None, 1) == -1
+    buf = (ctypes.c_uint64 * 8)()
+    assert lib.tidar_attn_stamps(ctypes.addressof(buf), -1) == -1

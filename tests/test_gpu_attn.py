@@ -367,3 +367,24 @@ def test_ten_calls_on_one_workspace_bitwise_equal(cfg):
         lses.append(lse.view(torch.int32).cpu().numpy())
     for i in range(1, 10):
         assert np.array_equal(outs[0], outs[i]) and np.array_equal(lses[0], lses[i])
+
+
+def test_timestamped_launch_is_the_same_computation(monkeypatch):
+    """TIDAR_ATTN_STAMPS=1 selects the timestamped instantiation of the main
+    kernel (bench.py --stamps): at the Qwen3-8B step's launch its output
+    equals the plain launch's bit for bit, and every workgroup's record is
+    ordered (entry <= first scores <= loop end <= stores acknowledged)."""
+    import ar_self_speculative_amd as tidar
+    c = config_attn(3, seed=2, layers=1)
+    monkeypatch.delenv("TIDAR_ATTN_STAMPS", raising=False)
+    base, _ = run_attn(c, with_lse=False)
+    monkeypatch.setenv("TIDAR_ATTN_STAMPS", "1")
+    out, _ = run_attn(c, with_lse=False)
+    assert np.array_equal(out, base)
+    r = tidar.attn_stamps(4096).astype(np.int64)
+    nwg = int(r[0, 7] >> 32)
+    assert 0 < nwg <= 4096
+    r = r[:nwg]
+    assert np.all(r[:, 0] <= r[:, 2]) and np.all(r[:, 2] <= r[:, 3]) and np.all(r[:, 3] <= r[:, 4])
+    assert np.all(r[:, 1] <= r[:, 5])
+    assert np.all((r[:, 7] & 0xFFFF) > 0)  # every workgroup of this launch had tiles
